@@ -1,0 +1,223 @@
+"""CPU oracle for the per-token NVFP4 path -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import this package.  The product library
+(``nvfp4_token_quantization_amd``) never imports it, and the two share no code.
+
+The arithmetic lives in ``nvfp4_oracle.c`` (plain C, built with
+``-ffp-contract=off`` and without fast-math so every fp32 step is one IEEE
+operation).  This module only marshals numpy arrays.
+
+Sources: the pages "miniTE报告：原生NVFP4训RL后期为何失稳，8×B300上提速1.37倍"
+(section NVFP4格式、两级缩放与转换误差), "Towards Blackwell-Native 8-bit and 4-bit
+RL: End-to-End MXFP8 and NVFP4 RL in Miles" (sections 速读, NVFP4格式背景,
+位级精确的量化器契约) and "TRIAGE: Direction-Aware Mismatch Stabilization of
+Native NVFP4 Reinforcement Learning" (section 前置知识, the decode formula
+x_hat = S * s_b * Q_E2M1(x / (S * s_b))).
+
+Every function here is pinned by the ``-m "not gpu"`` tests in
+``tests/test_oracle_*.py`` against library routines, closed forms, invariants
+and brute force.
+"""
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "nvfp4_oracle.c")
+_LIB = os.path.join(_HERE, "libnvfp4_oracle.so")
+
+GCC_FLAGS = ["-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp", "-ffp-contract=off",
+             "-fno-fast-math", "-fexcess-precision=standard", "-Wall"]
+
+
+def build(force=False):
+    """Compile the oracle with gcc (plain C, IEEE fp32, OpenMP)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        subprocess.check_call(["gcc"] + GCC_FLAGS + [_SRC, "-o", tmp, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        build()
+        L = ctypes.CDLL(_LIB)
+        P = ctypes.c_void_p
+        I64 = ctypes.c_int64
+        L.oracle_e2m1_value.argtypes = [ctypes.c_int]
+        L.oracle_e2m1_value.restype = ctypes.c_double
+        L.oracle_e4m3_value.argtypes = [ctypes.c_int]
+        L.oracle_e4m3_value.restype = ctypes.c_double
+        L.oracle_rne_sat_e2m1.argtypes = [ctypes.c_float]
+        L.oracle_rne_sat_e2m1.restype = ctypes.c_int
+        L.oracle_rne_sat_e4m3.argtypes = [ctypes.c_float]
+        L.oracle_rne_sat_e4m3.restype = ctypes.c_int
+        L.oracle_rne_sat_e2m1_array.argtypes = [P, I64, P]
+        L.oracle_rne_sat_e4m3_array.argtypes = [P, I64, P]
+        L.oracle_quantize_rows.argtypes = [P, I64, I64, P, P, P, P]
+        L.oracle_quantize_rows.restype = ctypes.c_int
+        L.oracle_quantize_weight.argtypes = [P, I64, I64, I64, P, P, P, P, P]
+        L.oracle_quantize_weight.restype = ctypes.c_int
+        L.oracle_dequantize.argtypes = [P, P, P, P, I64, I64, P]
+        L.oracle_gemm_entries.argtypes = [P, P, P, P, P, P, I64, P, P, P, I64, P, P]
+        L.oracle_gemm.argtypes = [P, P, P, I64, P, P, P, I64, I64, P, P]
+        L.oracle_grouped_gemm.argtypes = [P, P, P, P, P, I64, P, P, P, I64, I64, P, P]
+        _lib = L
+    return _lib
+
+
+def _p(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _c(a, dtype):
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+# ------------------------------------------------------------------ codecs --
+def e2m1_value(code):
+    """Value of a 4-bit E2M1 code (sign, 2 exponent bits, 1 mantissa bit)."""
+    return lib().oracle_e2m1_value(int(code))
+
+
+def e4m3_value(code):
+    """Value of an 8-bit E4M3 (OCP FN) code; NaN for 0x7F / 0xFF."""
+    return lib().oracle_e4m3_value(int(code))
+
+
+def e2m1_table():
+    return np.array([e2m1_value(c) for c in range(16)], dtype=np.float64)
+
+
+def e4m3_table():
+    return np.array([e4m3_value(c) for c in range(256)], dtype=np.float64)
+
+
+def rne_sat_e2m1(v):
+    """Non-negative E2M1 magnitude code (0..7) nearest to each fp32 v >= 0."""
+    v = _c(np.atleast_1d(v), np.float32)
+    out = np.empty(v.shape, np.uint8)
+    lib().oracle_rne_sat_e2m1_array(_p(v), v.size, _p(out))
+    return out
+
+
+def rne_sat_e4m3(v):
+    """Non-negative E4M3 code (0..0x7E) nearest to each fp32 v >= 0."""
+    v = _c(np.atleast_1d(v), np.float32)
+    out = np.empty(v.shape, np.uint8)
+    lib().oracle_rne_sat_e4m3_array(_p(v), v.size, _p(out))
+    return out
+
+
+# --------------------------------------------------------------- quantizer --
+def quantize_rows(x_bf16, amax_in=None):
+    """Per-token NVFP4: x_bf16 is uint16 bf16 bits [rows, k], k % 16 == 0.
+
+    Returns (q uint8 [rows, k/2], sb uint8 [rows, k/16], s float32 [rows]).
+    """
+    x = _c(x_bf16, np.uint16)
+    rows, k = x.shape
+    q = np.empty((rows, k // 2), np.uint8)
+    sb = np.empty((rows, k // 16), np.uint8)
+    s = np.empty((rows,), np.float32)
+    a = None if amax_in is None else _c(amax_in, np.float32)
+    rc = lib().oracle_quantize_rows(_p(x), rows, k, _p(a), _p(q), _p(sb), _p(s))
+    if rc != 0:
+        raise ValueError("oracle_quantize_rows: bad shape or non-finite input")
+    return q, sb, s
+
+
+def quantize_weight(w_bf16, amax_in=None):
+    """Per-tensor / per-expert NVFP4: w_bf16 uint16 [groups, rows, k].
+
+    Returns (q [groups, rows, k/2], sb [groups, rows, k/16], s float32 [groups],
+    amax float32 [groups]).
+    """
+    w = _c(w_bf16, np.uint16)
+    g, r, k = w.shape
+    q = np.empty((g, r, k // 2), np.uint8)
+    sb = np.empty((g, r, k // 16), np.uint8)
+    s = np.empty((g,), np.float32)
+    amax = np.empty((g,), np.float32)
+    a = None if amax_in is None else _c(amax_in, np.float32)
+    rc = lib().oracle_quantize_weight(_p(w), g, r, k, _p(a), _p(amax), _p(q), _p(sb), _p(s))
+    if rc != 0:
+        raise ValueError("oracle_quantize_weight: bad shape or non-finite input")
+    return q, sb, s, amax
+
+
+def dequantize(q, sb, s, s_index=None):
+    """x_hat = S * s_b * e2m1(q) in fp64; q [rows, k/2], sb [rows, k/16]."""
+    q = _c(q, np.uint8)
+    sb = _c(sb, np.uint8)
+    s = _c(s, np.float32)
+    rows = q.shape[0]
+    k = q.shape[1] * 2
+    si = None if s_index is None else _c(s_index, np.int64)
+    out = np.empty((rows, k), np.float64)
+    lib().oracle_dequantize(_p(q), _p(sb), _p(s), _p(si), rows, k, _p(out))
+    return out
+
+
+# -------------------------------------------------------------------- GEMM --
+def gemm(a, b):
+    """Exact Y_ref and error bound for Y = deq(A) . deq(B)^T.
+
+    a = (q [m, k/2], sb [m, k/16], s [m]); b = (q [n, k/2], sb [n, k/16], s [1]).
+    Returns (y_ref fp64 [m, n], bound fp64 [m, n]) where bound = sum_k |a_k b_k|.
+    """
+    aq, asb, as_ = (_c(a[0], np.uint8), _c(a[1], np.uint8), _c(a[2], np.float32))
+    bq, bsb, bs = (_c(b[0], np.uint8), _c(b[1], np.uint8), _c(np.atleast_1d(b[2]), np.float32))
+    m, n, k = aq.shape[0], bq.shape[0], aq.shape[1] * 2
+    y = np.empty((m, n), np.float64)
+    bound = np.empty((m, n), np.float64)
+    lib().oracle_gemm(_p(aq), _p(asb), _p(as_), m, _p(bq), _p(bsb), _p(bs), n, k, _p(y), _p(bound))
+    return y, bound
+
+
+def gemm_entries(a, b, a_row, b_row, b_scale):
+    """Exact (y_ref, bound) for a list of entries: A row a_row[i] against B row
+    b_row[i] (B flattened to [groups*n, k]) with B outer scale b_s[b_scale[i]]."""
+    aq, asb, as_ = (_c(a[0], np.uint8), _c(a[1], np.uint8), _c(a[2], np.float32))
+    bq, bsb, bs = (_c(b[0], np.uint8), _c(b[1], np.uint8), _c(np.atleast_1d(b[2]), np.float32))
+    k = aq.shape[-1] * 2
+    ar, br, bsi = _c(a_row, np.int64), _c(b_row, np.int64), _c(b_scale, np.int64)
+    cnt = ar.size
+    y = np.empty((cnt,), np.float64)
+    bound = np.empty((cnt,), np.float64)
+    lib().oracle_gemm_entries(_p(aq), _p(asb), _p(as_), _p(bq), _p(bsb), _p(bs), k,
+                              _p(ar), _p(br), _p(bsi), cnt, _p(y), _p(bound))
+    return y, bound
+
+
+def grouped_gemm(a, offsets, b, row_index=None, m_total=None):
+    """Exact (y_ref, bound) for the grouped GEMM over a contiguous per-expert
+    layout.  b = (q [g, n, k/2], sb [g, n, k/16], s [g]).  Rows at or past
+    offsets[g] are NaN in the returned arrays (not part of the product)."""
+    aq, asb, as_ = (_c(a[0], np.uint8), _c(a[1], np.uint8), _c(a[2], np.float32))
+    bq, bsb, bs = (_c(b[0], np.uint8), _c(b[1], np.uint8), _c(b[2], np.float32))
+    off = _c(offsets, np.int32)
+    groups, n, k = bq.shape[0], bq.shape[1], bq.shape[2] * 2
+    if m_total is None:
+        m_total = int(off[-1])
+    ri = None if row_index is None else _c(row_index, np.int32)
+    y = np.full((m_total, n), np.nan, np.float64)
+    bound = np.full((m_total, n), np.nan, np.float64)
+    lib().oracle_grouped_gemm(_p(aq), _p(asb), _p(as_), _p(ri), _p(off), groups, _p(bq), _p(bsb),
+                              _p(bs), n, k, _p(y), _p(bound))
+    return y, bound
+
+
+def gemm_within_bound(y, y_ref, bound, rel=1e-5):
+    """Acceptance: |Y - Y_ref| <= rel * sum_k |a_k b_k|, and Y is +-0 where the
+    bound is 0.  Returns a boolean mask of passing entries."""
+    y = np.asarray(y, np.float64)
+    return np.abs(y - y_ref) <= rel * bound
