@@ -1,0 +1,183 @@
+/*
+ * nvfp4.h -- C ABI of libnvfp4.so: per-token NVFP4 quantization and the
+ * block-scaled W4A4 linear it feeds, for AMD Instinct MI355X (gfx950).
+ *
+ * NVFP4 as used here (see the pages named in each declaration):
+ *   x_hat = S * s_b * e2m1(q)
+ *   q   : 4-bit E2M1 code (sign, 2 exponent bits, 1 mantissa bit), two per
+ *         byte, element 2i in the low nibble of byte i;
+ *   s_b : one E4M3 (OCP "FN", max 448) block scale per 16 consecutive
+ *         elements along the contraction axis K;
+ *   S   : FP32 outer scale, per row (per token) for activations, per tensor
+ *         or per expert for weights.
+ *
+ * Quantization contract (one result is correct; it is reproduced bit for bit):
+ *   S     = fl32(amax / 2688)                         (2688 = 6 * 448)
+ *   s_b   = RNE_SAT_E4M3(fl32(a_b / fl32(6 * S)))      (0 when S == 0)
+ *   d     = fl32(S * s_b)
+ *   code  = sign(x) | RNE_SAT_E2M1(|fl32(x * fl32(1 / d))|)
+ *           (magnitude 0 when d == 0 or x == +-0)
+ * RNE_SAT rounds to the nearest finite code value with ties to the even code
+ * and saturates (values above the maximum and +inf give the maximum).  amax
+ * is the row (or group) max of |x|; a_b is the block max of |x|.
+ *
+ * Layouts (all row-major, canonical, no padding or swizzling):
+ *   bf16 input  [rows, k]          -> q [rows, k/2] u8, sb [rows, k/16] u8
+ *   per-token S [rows] f32;  weight S [groups] f32
+ *   GEMM: Y[m, n] = sum_k x_hat_A[m, k] * x_hat_B[n, k]  (both K-major,
+ *   blocks along K), Y fp32 [m, n] row-major.
+ *
+ * Conventions for every call:
+ *   - Pointers are device pointers owned by the caller.  The library never
+ *     allocates, frees or keeps them.  Inputs are read-only; outputs are
+ *     overwritten; inputs and outputs must not overlap.
+ *   - `stream` is a hipStream_t passed as void* (NULL = default stream).
+ *     Calls are asynchronous and never synchronize the host.  The host never
+ *     reads device data (grouped GEMM offsets stay on the device).
+ *   - Return value: NVFP4_SUCCESS or an error code.  Argument errors are
+ *     detected before any HIP call and launch nothing.  NVFP4_ERROR_LAUNCH
+ *     reports a failed launch (hipGetLastError).  NVFP4_ERROR_ARCH: the
+ *     current device is not gfx950.
+ *   - Alignment: tensor pointers must be 16-byte aligned (fp32 scale
+ *     vectors 4-byte aligned).
+ *   - Inputs must be finite; non-finite bf16 inputs give unspecified codes
+ *     (no fault).  Stateless and re-entrant; calls on one stream are ordered.
+ */
+#ifndef NVFP4_H
+#define NVFP4_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define NVFP4_SUCCESS 0
+#define NVFP4_ERROR_INVALID_VALUE 1     /* null pointer, negative size, zero groups */
+#define NVFP4_ERROR_UNSUPPORTED_SHAPE 2 /* k % 16 != 0, or a size past a stated limit */
+#define NVFP4_ERROR_MISALIGNED 3        /* pointer alignment below the stated minimum */
+#define NVFP4_ERROR_LAUNCH 4            /* kernel launch failed */
+#define NVFP4_ERROR_ARCH 5              /* current device is not gfx950 */
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+int nvfp4_version(void);
+
+/* Static string naming a status code (never NULL). */
+const char* nvfp4_status_string(int status);
+
+/*
+ * Per-token NVFP4 activation quantization.
+ *
+ * Defined by: "Towards Blackwell-Native 8-bit and 4-bit RL: End-to-End MXFP8
+ * and NVFP4 RL in Miles", section 速读 (X ~ s_token * s_block * X_FP4, 16 E2M1
+ * values per E4M3 block scale) and section 单Token缩放的在线计算实现 (the FP32
+ * per-token scale is computed online inside the quantize call, which returns
+ * packed FP4, E4M3 block scales and the per-token scale together); decode
+ * formula on "TRIAGE: Direction-Aware Mismatch Stabilization of Native NVFP4
+ * Reinforcement Learning", section 前置知识.  Amax reuse ("miniTE报告", section
+ * Transformer Engine路径优化) is the amax_in argument.
+ *
+ *   x_bf16  [rows, k] bf16 bit patterns, k % 16 == 0 (k may be 0)
+ *   amax_in NULL: amax = max_k |x[r, k]| computed here.
+ *           else [rows] f32: amax of row r is amax_in[r] (the producer's
+ *           statistic; bits are a function of (x, amax_in)).
+ *   q       [rows, k/2] u8 out;  sb [rows, k/16] u8 out;  s [rows] f32 out (S)
+ * Each row's output depends only on that row (batch invariant).
+ * Errors: INVALID_VALUE (rows or k < 0; null x, q, sb or s when there is work),
+ * UNSUPPORTED_SHAPE (k % 16 != 0), MISALIGNED, ARCH, LAUNCH.
+ */
+int nvfp4_quantize_rows(const uint16_t* x_bf16, int64_t rows, int64_t k, const float* amax_in,
+                        uint8_t* q, uint8_t* sb, float* s, void* stream);
+
+/*
+ * Weight NVFP4 quantization with a per-tensor or per-expert FP32 outer scale.
+ *
+ * Defined by: "miniTE报告" section NVFP4格式、两级缩放与转换误差 (the outer
+ * scale may be per tensor, per expert or per row) and the Miles page, section
+ * 并行度与张量转换的一致性契约 (fused gate/up weights share one FP32 scale:
+ * pass the fused [2I, H] expert weight as one group); weights use 1D 1x16
+ * blocks along K (Miles page, recipe under 补充细节, 2D quantization disabled).
+ *
+ *   w_bf16   [groups, rows_per_group, k] bf16 bits, k % 16 == 0
+ *   amax_in  NULL: amax[g] = max |w[g]| reduced here (into amax_out).
+ *            else [groups] f32 used as the group amax.
+ *   amax_out [groups] f32 out: the group amax (required when amax_in is
+ *            NULL, where it also serves as the reduction target; optional
+ *            otherwise, then a copy of amax_in).
+ *   q [groups*rows_per_group, k/2] u8 out; sb [groups*rows_per_group, k/16] u8
+ *   out; s [groups] f32 out (S per group).
+ * Each row is encoded exactly as nvfp4_quantize_rows would encode it with
+ * amax_in set to its group's amax.  Errors as for nvfp4_quantize_rows, plus
+ * INVALID_VALUE for groups < 1 or a missing amax_out.
+ */
+int nvfp4_quantize_weight(const uint16_t* w_bf16, int64_t groups, int64_t rows_per_group,
+                          int64_t k, const float* amax_in, float* amax_out, uint8_t* q,
+                          uint8_t* sb, float* s, void* stream);
+
+/*
+ * Dense block-scaled W4A4 GEMM: Y = deq(A) . deq(B)^T with the per-token
+ * scale and the weight scale applied in the epilogue, Y = S_A[m] * S_B *
+ * sum_k (s_bA q_A)(s_bB q_B).
+ *
+ * Defined by: the Miles page, section 速读 (X ~ s_token * s_block * X_FP4) and
+ * 实验结果 item 10 (the per-token FP32 scale belongs in the GEMM epilogue, not
+ * a separate op); blocks run along the contraction axis (Miles page, section
+ * 案例研究：MXFP8 MLA投影张量).
+ *
+ *   A: a_q [m, k/2], a_sb [m, k/16], a_s [m] (per-token S)
+ *   B: b_q [n, k/2], b_sb [n, k/16], b_s [1] (per-tensor S)
+ *   y  [m, n] f32 out
+ * Accuracy: each |Y - Y_exact| <= 1e-5 * sum_k |a_k b_k| (fp32 accumulation
+ * of exactly decoded operands; the summation order is not specified).
+ * Errors: INVALID_VALUE, UNSUPPORTED_SHAPE (k % 16 != 0), MISALIGNED, ARCH,
+ * LAUNCH.  m, n or k == 0 are allowed (k == 0 writes zeros).
+ */
+int nvfp4_gemm(const uint8_t* a_q, const uint8_t* a_sb, const float* a_s, int64_t m,
+               const uint8_t* b_q, const uint8_t* b_sb, const float* b_s, int64_t n, int64_t k,
+               float* y, void* stream);
+
+/*
+ * Grouped (MoE) block-scaled W4A4 GEMM over a contiguous per-expert layout
+ * with device-side metadata.
+ *
+ * Defined by: "miniTE报告" section Transformer Engine路径优化 (contiguous
+ * layouts, device-side metadata, amax reuse and grouped GEMM for the
+ * per-token NVFP4 path) and the Miles page, section 配方2 (NVFP4 on the MoE
+ * expert layers).
+ *
+ *   A: a_q [a_rows, k/2], a_sb [a_rows, k/16], a_s [a_rows]
+ *   row_index NULL: output row i reads A row i (then a_rows >= m_total).
+ *             else [m_total] i32 device: output row i reads A row
+ *             row_index[i] -- a token quantized once serves all its routed
+ *             copies.  Indices outside [0, a_rows) read as zero rows.
+ *   offsets   [groups+1] i32 device, non-decreasing: expert g owns output
+ *             rows [offsets[g], offsets[g+1]).  Values are clamped to
+ *             [0, m_total]; rows at or past offsets[groups] are not written.
+ *   B: b_q [groups, n, k/2], b_sb [groups, n, k/16], b_s [groups] (per expert)
+ *   y  [m_total, n] f32 out
+ * Accuracy as nvfp4_gemm.  groups <= 4096.
+ * Errors: INVALID_VALUE (groups < 1, negative sizes, null pointers),
+ * UNSUPPORTED_SHAPE (k % 16 != 0, groups > 4096), MISALIGNED, ARCH, LAUNCH.
+ */
+int nvfp4_grouped_gemm(const uint8_t* a_q, const uint8_t* a_sb, const float* a_s, int64_t a_rows,
+                       const int32_t* row_index, int64_t m_total, const int32_t* offsets,
+                       int64_t groups, const uint8_t* b_q, const uint8_t* b_sb, const float* b_s,
+                       int64_t n, int64_t k, float* y, void* stream);
+
+/*
+ * Codec self-test hooks: apply the device rounding functions the quantizer
+ * uses to arbitrary fp32 inputs, so tests can sweep every bit pattern.
+ *   nvfp4_debug_encode_e2m1: code[i] = 4-bit E2M1 code (sign | RNE_SAT
+ *     magnitude) of v[i]; +-inf saturate; NaN inputs give unspecified codes.
+ *   nvfp4_debug_encode_e4m3: code[i] = RNE_SAT E4M3 code of v[i] >= 0
+ *     (+inf saturates to 0x7E); negative or NaN inputs give unspecified codes.
+ * v [n] f32 device, code [n] u8 device.  Errors as above.
+ */
+int nvfp4_debug_encode_e2m1(const float* v, int64_t n, uint8_t* code, void* stream);
+int nvfp4_debug_encode_e4m3(const float* v, int64_t n, uint8_t* code, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NVFP4_H */

@@ -1,0 +1,229 @@
+"""Per-token NVFP4 quantization and block-scaled W4A4 GEMM on MI355X (gfx950).
+
+Thin Python binding over the C ABI of ``libnvfp4.so`` (declared in
+``include/nvfp4.h``).  Every step of the path runs in the library's HIP
+kernels; this module only checks tensor metadata, allocates outputs with
+torch and passes device pointers plus torch's current stream.  There is no
+CPU fallback: if the library is missing or the device is not gfx950 the
+calls raise.
+
+Functions keep the C names:
+
+  nvfp4_quantize_rows(x, amax_in=None)            -> (q, sb, s)
+  nvfp4_quantize_weight(w, amax_in=None)          -> (q, sb, s, amax)
+  nvfp4_gemm(a, b)                                -> y
+  nvfp4_grouped_gemm(a, offsets, b, row_index=None, m_total=None) -> y
+  nvfp4_debug_encode_e2m1(v), nvfp4_debug_encode_e4m3(v)   (codec hooks)
+
+Layouts (all row-major): x bf16 [rows, k]; q uint8 [rows, k/2] with element
+2i in the low nibble; sb uint8 [rows, k/16] (E4M3 codes); s float32 [rows]
+(per-token) or [groups] (weights); a GEMM operand is the tuple (q, sb, s).
+"""
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libnvfp4.so")
+
+SUCCESS = 0
+_lib = None
+
+
+class NVFP4Error(RuntimeError):
+    def __init__(self, fn, status):
+        self.status = status
+        super().__init__("%s failed: %s (status %d)" % (fn, status_string(status), status))
+
+
+def lib():
+    """Load libnvfp4.so (built in-tree by ``__graft_entry__.build()``)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError("libnvfp4.so is not built: run __graft_entry__.build() "
+                               "(or python -m nvfp4_token_quantization_amd.build)")
+        L = ctypes.CDLL(LIB_PATH)
+        P, I64 = ctypes.c_void_p, ctypes.c_int64
+        L.nvfp4_version.restype = ctypes.c_int
+        L.nvfp4_status_string.argtypes = [ctypes.c_int]
+        L.nvfp4_status_string.restype = ctypes.c_char_p
+        L.nvfp4_quantize_rows.argtypes = [P, I64, I64, P, P, P, P, P]
+        L.nvfp4_quantize_weight.argtypes = [P, I64, I64, I64, P, P, P, P, P, P]
+        L.nvfp4_gemm.argtypes = [P, P, P, I64, P, P, P, I64, I64, P, P]
+        L.nvfp4_grouped_gemm.argtypes = [P, P, P, I64, P, I64, P, I64, P, P, P, I64, I64, P, P]
+        L.nvfp4_debug_encode_e2m1.argtypes = [P, I64, P, P]
+        L.nvfp4_debug_encode_e4m3.argtypes = [P, I64, P, P]
+        for f in ("nvfp4_quantize_rows", "nvfp4_quantize_weight", "nvfp4_gemm",
+                  "nvfp4_grouped_gemm", "nvfp4_debug_encode_e2m1", "nvfp4_debug_encode_e4m3"):
+            getattr(L, f).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def version():
+    return lib().nvfp4_version()
+
+
+def status_string(status):
+    return lib().nvfp4_status_string(int(status)).decode()
+
+
+def _check(fn, status):
+    if status != SUCCESS:
+        raise NVFP4Error(fn, status)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(dev):
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def _dev(t, name, dtypes, ndim=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if not t.is_cuda:
+        raise ValueError("%s must be on a GPU (got %s)" % (name, t.device))
+    if t.dtype not in dtypes:
+        raise TypeError("%s must have dtype in %s (got %s)" % (name, dtypes, t.dtype))
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError("%s must have %d dims (got %s)" % (name, ndim, tuple(t.shape)))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    return t
+
+
+_BF16 = (torch.bfloat16, torch.int16, torch.uint16)
+
+
+def nvfp4_quantize_rows(x, amax_in=None, out=None):
+    """Per-token NVFP4 of bf16 rows x [rows, k] (k % 16 == 0).
+
+    amax_in: optional float32 [rows], the producer's row amax (amax reuse).
+    out: optional preallocated (q, sb, s).  Returns (q, sb, s).
+    """
+    _dev(x, "x", _BF16, 2)
+    rows, k = x.shape
+    dev = x.device
+    if out is None:
+        q = torch.empty((rows, k // 2), dtype=torch.uint8, device=dev)
+        sb = torch.empty((rows, k // 16), dtype=torch.uint8, device=dev)
+        s = torch.empty((rows,), dtype=torch.float32, device=dev)
+    else:
+        q, sb, s = out
+    if amax_in is not None:
+        _dev(amax_in, "amax_in", (torch.float32,), 1)
+        if amax_in.numel() != rows:
+            raise ValueError("amax_in must have one entry per row")
+    st = lib().nvfp4_quantize_rows(_ptr(x), rows, k, _ptr(amax_in), _ptr(q), _ptr(sb), _ptr(s),
+                                   _stream(dev))
+    _check("nvfp4_quantize_rows", st)
+    return q, sb, s
+
+
+def nvfp4_quantize_weight(w, amax_in=None, out=None):
+    """Per-tensor (groups == 1) or per-expert NVFP4 of bf16 w [groups, rows, k].
+
+    Returns (q [groups, rows, k/2], sb [groups, rows, k/16], s [groups],
+    amax [groups]).
+    """
+    _dev(w, "w", _BF16, 3)
+    g, r, k = w.shape
+    dev = w.device
+    if out is None:
+        q = torch.empty((g, r, k // 2), dtype=torch.uint8, device=dev)
+        sb = torch.empty((g, r, k // 16), dtype=torch.uint8, device=dev)
+        s = torch.empty((g,), dtype=torch.float32, device=dev)
+        amax = torch.empty((g,), dtype=torch.float32, device=dev)
+    else:
+        q, sb, s, amax = out
+    if amax_in is not None:
+        _dev(amax_in, "amax_in", (torch.float32,), 1)
+        if amax_in.numel() != g:
+            raise ValueError("amax_in must have one entry per group")
+    st = lib().nvfp4_quantize_weight(_ptr(w), g, r, k, _ptr(amax_in), _ptr(amax), _ptr(q),
+                                     _ptr(sb), _ptr(s), _stream(dev))
+    _check("nvfp4_quantize_weight", st)
+    return q, sb, s, amax
+
+
+def _operand(t, name):
+    q, sb, s = t
+    _dev(q, name + ".q", (torch.uint8,))
+    _dev(sb, name + ".sb", (torch.uint8,))
+    _dev(s, name + ".s", (torch.float32,))
+    return q, sb, s
+
+
+def nvfp4_gemm(a, b, out=None):
+    """Y = deq(A) . deq(B)^T, fp32 [m, n].  a = (q [m, k/2], sb [m, k/16],
+    s [m]); b = (q [n, k/2], sb [n, k/16], s [1])."""
+    aq, asb, as_ = _operand(a, "a")
+    bq, bsb, bs = _operand(b, "b")
+    m, n = aq.shape[0], bq.shape[-2] if bq.dim() == 3 else bq.shape[0]
+    k = aq.shape[-1] * 2
+    if bq.shape[-1] * 2 != k:
+        raise ValueError("A and B must have the same k")
+    dev = aq.device
+    y = torch.empty((m, n), dtype=torch.float32, device=dev) if out is None else out
+    st = lib().nvfp4_gemm(_ptr(aq), _ptr(asb), _ptr(as_), m, _ptr(bq), _ptr(bsb), _ptr(bs), n, k,
+                          _ptr(y), _stream(dev))
+    _check("nvfp4_gemm", st)
+    return y
+
+
+def nvfp4_grouped_gemm(a, offsets, b, row_index=None, m_total=None, out=None):
+    """Grouped GEMM over a contiguous per-expert layout.
+
+    a = (q [a_rows, k/2], sb [a_rows, k/16], s [a_rows]);
+    offsets int32 [groups+1] (device); b = (q [groups, n, k/2],
+    sb [groups, n, k/16], s [groups]); row_index optional int32 [m_total].
+    m_total defaults to len(row_index) or a_rows (the host never reads
+    offsets).  Rows at or past offsets[groups] of the output are not written.
+    """
+    aq, asb, as_ = _operand(a, "a")
+    bq, bsb, bs = _operand(b, "b")
+    _dev(offsets, "offsets", (torch.int32,), 1)
+    if bq.dim() != 3:
+        raise ValueError("b.q must be [groups, n, k/2]")
+    groups, n, k = bq.shape[0], bq.shape[1], bq.shape[2] * 2
+    if offsets.numel() != groups + 1:
+        raise ValueError("offsets must have groups + 1 entries")
+    a_rows = aq.shape[0]
+    if row_index is not None:
+        _dev(row_index, "row_index", (torch.int32,), 1)
+        if m_total is None:
+            m_total = row_index.numel()
+        elif row_index.numel() < m_total:
+            raise ValueError("row_index must have m_total entries")
+    elif m_total is None:
+        m_total = a_rows
+    dev = aq.device
+    y = torch.empty((m_total, n), dtype=torch.float32, device=dev) if out is None else out
+    st = lib().nvfp4_grouped_gemm(_ptr(aq), _ptr(asb), _ptr(as_), a_rows, _ptr(row_index),
+                                  m_total, _ptr(offsets), groups, _ptr(bq), _ptr(bsb), _ptr(bs),
+                                  n, k, _ptr(y), _stream(dev))
+    _check("nvfp4_grouped_gemm", st)
+    return y
+
+
+def nvfp4_debug_encode_e2m1(v):
+    """Device E2M1 code (sign | RNE_SAT magnitude) of each float32 in v."""
+    _dev(v, "v", (torch.float32,))
+    out = torch.empty(v.shape, dtype=torch.uint8, device=v.device)
+    _check("nvfp4_debug_encode_e2m1",
+           lib().nvfp4_debug_encode_e2m1(_ptr(v), v.numel(), _ptr(out), _stream(v.device)))
+    return out
+
+
+def nvfp4_debug_encode_e4m3(v):
+    """Device RNE_SAT E4M3 code of each non-negative float32 in v."""
+    _dev(v, "v", (torch.float32,))
+    out = torch.empty(v.shape, dtype=torch.uint8, device=v.device)
+    _check("nvfp4_debug_encode_e4m3",
+           lib().nvfp4_debug_encode_e4m3(_ptr(v), v.numel(), _ptr(out), _stream(v.device)))
+    return out

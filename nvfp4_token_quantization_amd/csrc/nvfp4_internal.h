@@ -1,0 +1,88 @@
+// nvfp4_internal.h -- device helpers and host plumbing shared by the kernels
+// of libnvfp4.so (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "nvfp4.h"
+
+namespace nvfp4 {
+
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __fp16 hp16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+// ------------------------------------------------------------ E4M3 codec --
+// RNE_SAT onto E4M3 (OCP FN, bias 7, max 448) for v >= 0 or +inf.  Values at
+// or above 448 saturate; below 2^-6 the grid is the subnormal step 2^-9 and
+// round-to-nearest-even on v * 2^9 is exact; otherwise the fp32 mantissa is
+// rounded to 3 bits with ties to even (a carry moves into the exponent).
+__device__ __forceinline__ uint32_t e4m3_encode(float v) {
+  if (!(v < 448.0f)) return 0x7Eu;
+  if (v < 0.015625f) return (uint32_t)__builtin_rintf(v * 512.0f);
+  uint32_t u = __float_as_uint(v);
+  u += 0x7FFFFu + ((u >> 20) & 1u);
+  return (u >> 20) - (120u << 3);
+}
+
+// Exact fp32 value of an E4M3 code 0..0x7E.
+__device__ __forceinline__ float e4m3_decode(uint32_t c) {
+  uint32_t e = c >> 3, m = c & 7u;
+  float sub = (float)m * 0.001953125f;  // m * 2^-9
+  float nrm = __uint_as_float(((e + 120u) << 23) | (m << 20));
+  return e ? nrm : sub;
+}
+
+// ------------------------------------------------------------ E2M1 codec --
+// Two fp32 values -> two E2M1 codes in byte `sel` of `old` (src0 in the low
+// nibble).  gfx950's converter with scale 1.0 rounds to nearest even with
+// ties to the even code, saturates to +-6 (also for +-inf) and copies the
+// sign (including -0 and negative denormals); the exhaustive sweep test
+// checks this against the oracle for every fp32 bit pattern.
+template <int SEL>
+__device__ __forceinline__ uint32_t e2m1_encode2(uint32_t old, float a, float b) {
+  return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, a, b, 1.0f, SEL);
+}
+
+// ---------------------------------------------------- wave-level max (u32) --
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_mov(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+
+// Max over aligned groups of L lanes (L = 16, 32 or 64) of a wave64; every
+// lane of a group receives the group's max.  DPP quad permutes and row
+// mirrors inside each 16-lane row, ds_swizzle (xor 16) across row pairs and
+// readlane across the two halves of the wave.
+template <int L>
+__device__ __forceinline__ uint32_t group_max_u32(uint32_t v) {
+  v = max(v, dpp_mov<0xB1>(v));   // quad_perm [1,0,3,2]
+  v = max(v, dpp_mov<0x4E>(v));   // quad_perm [2,3,0,1]
+  v = max(v, dpp_mov<0x141>(v));  // row_half_mirror
+  v = max(v, dpp_mov<0x140>(v));  // row_mirror
+  if (L >= 32) v = max(v, (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x401F));
+  if (L >= 64) {
+    uint32_t a = (uint32_t)__builtin_amdgcn_readlane((int)v, 0);
+    uint32_t b = (uint32_t)__builtin_amdgcn_readlane((int)v, 32);
+    v = max(a, b);
+  }
+  return v;
+}
+
+}  // namespace nvfp4
+
+// ------------------------------------------------------------- host side --
+namespace nvfp4host {
+
+inline bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
+
+// Returns NVFP4_SUCCESS when the current device is gfx950 (cached per device).
+int check_arch();
+
+// Maps the last HIP launch error to a status.
+int launch_status();
+
+}  // namespace nvfp4host

@@ -1,0 +1,121 @@
+"""Host-side checks of the C ABI (no GPU needed).
+
+- libnvfp4.so loads and exports every function include/nvfp4.h declares;
+- argument errors return the documented status before any HIP call
+  (null pointers, negative sizes, k % 16 != 0, misaligned pointers, zero
+  groups), and empty problems return success without launching.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "nvfp4.h")
+
+OK, INVALID, SHAPE, MISALIGNED = 0, 1, 2, 3
+
+
+@pytest.fixture(scope="module")
+def L():
+    import nvfp4_token_quantization_amd as nv
+    return nv.lib()
+
+
+def declared_functions():
+    txt = open(HEADER).read()
+    return re.findall(r"^(?:int|const char\*)\s+(nvfp4_\w+)\(", txt, re.M)
+
+
+def test_header_declares_the_boundary():
+    names = set(declared_functions())
+    for n in ("nvfp4_quantize_rows", "nvfp4_quantize_weight", "nvfp4_gemm", "nvfp4_grouped_gemm",
+              "nvfp4_status_string", "nvfp4_version"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(L):
+    for name in declared_functions():
+        assert hasattr(L, name), name
+
+
+def test_status_strings_and_version(L):
+    import nvfp4_token_quantization_amd as nv
+    assert nv.version() == 100
+    for st in range(6):
+        assert nv.status_string(st)
+    assert nv.status_string(99) == "unknown status"
+
+
+FAKE = 0x10000          # 16-byte aligned, never dereferenced (errors return first)
+FAKE_ODD = 0x10001
+
+
+def P(v):
+    return ctypes.c_void_p(v)
+
+
+def test_quantize_rows_argument_errors(L):
+    f = L.nvfp4_quantize_rows
+    assert f(P(FAKE), -1, 16, None, P(FAKE), P(FAKE), P(FAKE), None) == INVALID
+    assert f(P(FAKE), 4, -16, None, P(FAKE), P(FAKE), P(FAKE), None) == INVALID
+    assert f(P(FAKE), 4, 24, None, P(FAKE), P(FAKE), P(FAKE), None) == SHAPE
+    assert f(None, 4, 16, None, P(FAKE), P(FAKE), P(FAKE), None) == INVALID
+    assert f(P(FAKE), 4, 16, None, None, P(FAKE), P(FAKE), None) == INVALID
+    assert f(P(FAKE), 4, 16, None, P(FAKE), None, P(FAKE), None) == INVALID
+    assert f(P(FAKE), 4, 16, None, P(FAKE), P(FAKE), None, None) == INVALID
+    assert f(P(FAKE_ODD), 4, 16, None, P(FAKE), P(FAKE), P(FAKE), None) == MISALIGNED
+    assert f(P(FAKE), 4, 16, None, P(FAKE + 8), P(FAKE), P(FAKE), None) == MISALIGNED
+    # nothing to do: success without touching the device
+    assert f(None, 0, 16, None, None, None, None, None) == OK
+
+
+def test_quantize_weight_argument_errors(L):
+    f = L.nvfp4_quantize_weight
+    a = P(FAKE)
+    assert f(a, 0, 4, 16, None, a, a, a, a, None) == INVALID        # zero groups
+    assert f(a, 2, -1, 16, None, a, a, a, a, None) == INVALID
+    assert f(a, 2, 4, 40, None, a, a, a, a, None) == SHAPE
+    assert f(a, 2, 4, 16, None, None, a, a, a, None) == INVALID     # no amax target
+    assert f(a, 2, 4, 16, None, a, a, a, None, None) == INVALID     # no s
+    assert f(None, 2, 4, 16, None, a, a, a, a, None) == INVALID
+    assert f(P(FAKE_ODD), 2, 4, 16, None, a, a, a, a, None) == MISALIGNED
+
+
+def test_gemm_argument_errors(L):
+    f = L.nvfp4_gemm
+    a = P(FAKE)
+    assert f(a, a, a, -1, a, a, a, 8, 16, a, None) == INVALID
+    assert f(a, a, a, 8, a, a, a, 8, 20, a, None) == SHAPE
+    assert f(a, a, a, 8, a, a, a, 8, 16, None, None) == INVALID
+    assert f(None, a, a, 8, a, a, a, 8, 16, a, None) == INVALID
+    assert f(a, a, a, 8, a, P(FAKE + 4), a, 8, 16, a, None) == MISALIGNED
+    assert f(None, None, None, 0, None, None, None, 8, 16, None, None) == OK  # m == 0
+
+
+def test_grouped_gemm_argument_errors(L):
+    f = L.nvfp4_grouped_gemm
+    a = P(FAKE)
+    assert f(a, a, a, 8, None, 8, a, 0, a, a, a, 8, 16, a, None) == INVALID    # groups 0
+    assert f(a, a, a, 8, None, 8, a, 2000, a, a, a, 8, 16, a, None) == SHAPE   # > 1024 groups
+    assert f(a, a, a, 8, None, 8, a, 2, a, a, a, 8, 24, a, None) == SHAPE
+    assert f(a, a, a, 8, None, 8, None, 2, a, a, a, 8, 16, a, None) == INVALID  # no offsets
+    assert f(a, a, a, 4, None, 8, a, 2, a, a, a, 8, 16, a, None) == INVALID     # a_rows < m_total
+    assert f(a, a, a, 8, P(FAKE + 2), 8, a, 2, a, a, a, 8, 16, a, None) == MISALIGNED
+    assert f(None, None, None, 0, None, 0, None, 2, None, None, None, 8, 16, None, None) == OK
+
+
+def test_debug_hooks_argument_errors(L):
+    assert L.nvfp4_debug_encode_e2m1(None, 4, P(FAKE), None) == INVALID
+    assert L.nvfp4_debug_encode_e4m3(P(FAKE), -1, P(FAKE), None) == INVALID
+    assert L.nvfp4_debug_encode_e4m3(P(FAKE + 1), 4, P(FAKE), None) == MISALIGNED
+    assert L.nvfp4_debug_encode_e2m1(None, 0, None, None) == OK
+
+
+def test_binding_fails_loudly_without_gpu_tensors():
+    import torch
+
+    import nvfp4_token_quantization_amd as nv
+    with pytest.raises(ValueError):
+        nv.nvfp4_quantize_rows(torch.zeros((4, 16), dtype=torch.bfloat16))  # CPU tensor
