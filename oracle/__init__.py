@@ -52,6 +52,7 @@ def lib():
         L = ctypes.CDLL(_LIB)
         P = ctypes.c_void_p
         I64 = ctypes.c_int64
+        L.oracle_threads.restype = ctypes.c_int
         L.oracle_e2m1_value.argtypes = [ctypes.c_int]
         L.oracle_e2m1_value.restype = ctypes.c_double
         L.oracle_e4m3_value.argtypes = [ctypes.c_int]
@@ -80,6 +81,11 @@ def _p(a):
 
 def _c(a, dtype):
     return np.ascontiguousarray(a, dtype=dtype)
+
+
+def threads():
+    """OpenMP threads the oracle's parallel loops use."""
+    return lib().oracle_threads()
 
 
 # ------------------------------------------------------------------ codecs --

@@ -45,6 +45,10 @@
 #include <stdint.h>
 #include <string.h>
 #include <math.h>
+#include <omp.h>
+
+/* number of OpenMP threads the parallel loops below use */
+int oracle_threads(void) { return omp_get_max_threads(); }
 
 /* ---------------------------------------------------------------- codecs -- */
 
