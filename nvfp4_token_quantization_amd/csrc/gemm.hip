@@ -22,21 +22,26 @@
 //       a bias difference of 8, subnormal codes included)
 //   product = e2m1 * s_b = u, exact and normal in fp16.
 //
-// Tiling: 256 threads = 2 x 2 waves, each wave owns TM x TN tiles of 32 x 32
-// (v_mfma_f32_32x32x16_f16).  A K stage is 128 elements: per row 64 bytes
-// of codes and 8 scale bytes, staged in LDS (double buffered, rows padded to
-// avoid bank conflicts).  Lane group h = lane / 32 of a wave takes the K
-// elements [64h, 64h+64) of the stage for both A and B; the MFMA's K order
-// inside a stage is therefore a permutation, identical for A and B, which
-// leaves the dot products unchanged.
+// Tiling (measured on MI355X: one wave per SIMD with a 128 x 128 tile and
+// no LDS round trip beats LDS-staged 2x2-wave blocks): one wave per block,
+// the block tile is the wave's 4 x 4 tiles of v_mfma_f32_32x32x16_f16 with
+// 256 fp32 accumulators.  A K stage is 128 elements; lane (li, h) loads, for
+// each 32-row slab of A and B, the 32 code bytes [32h, 32h + 32) of the row's
+// 64 and the dword of the 4 block scales that cover them, one stage ahead into
+// a register double buffer.  Lane half h therefore feeds the K elements
+// [64h, 64h + 64) of every stage to the MFMAs of both operands: a permutation
+// of K that is the same for A and B, so the dot products are unchanged.
+//
+// Tile order: blocks are dealt round-robin to the 8 XCDs; the grid is split
+// into 8 regions (one per XCD, along M for grouped GEMMs) so each XCD's L2
+// serves one region.  Grouped GEMMs derive the per-expert m-tile prefix from
+// the device offsets in every block, and ragged expert tiles run only their
+// non-empty 32-row slabs.
 #include "nvfp4_internal.h"
 
 namespace nvfp4 {
 
 constexpr int BK = 128;          // K elements per stage
-constexpr int ROWB = BK / 2;     // code bytes per row per stage
-constexpr int SROW = 80;         // LDS row stride for codes (64 + 16 pad)
-constexpr int SCB = BK / 16;     // scale bytes per row per stage
 constexpr int MAX_GROUPS = 1024;
 
 struct GemmArgs {
@@ -54,6 +59,7 @@ struct GemmArgs {
   int64_t n, k;
   float* y;
   int tiles_n;
+  int xcd_n;  // XCD regions along N (8 / xcd_n along M), register-direct kernel
 };
 
 __device__ __forceinline__ f16x2 as_h2(uint32_t v) { return __builtin_bit_cast(f16x2, v); }
@@ -77,26 +83,6 @@ __device__ __forceinline__ f16x2 scale_pair(uint32_t scales4, int blk) {
   return as_h2((c << 7) | (c << 23));
 }
 
-// Global -> register staging of one K stage for BM rows of A and BN rows of B.
-template <int BM, int BN, bool FAST>
-struct Stage {
-  static constexpr int ACH = BM * 4 / 256;  // 16-byte chunks of codes per thread (A)
-  static constexpr int BCH = BN * 4 / 256;
-  uint4 a[ACH];
-  uint4 b[BCH];
-  uint2 as;  // 8 scale bytes of one A row (threads < BM)
-  uint2 bs;  // 8 scale bytes of one B row (threads < BN)
-};
-
-// Row pointers of the tile, computed once per tile.
-template <int BM, int BN>
-struct TileRows {
-  int64_t arow[BM * 4 / 256];  // A source row per code chunk (-1: zero)
-  int64_t brow[BN * 4 / 256];
-  int64_t arow_s;              // A source row for the scale bytes (threads < BM)
-  int64_t brow_s;
-};
-
 // 8-byte load of bytes [off, off + 8) of a row with `valid` bytes (K tail):
 // bytes past `valid` read as zero and are never fetched.  `row + off` must be
 // 8-byte aligned when the 8 bytes are all valid.
@@ -108,112 +94,180 @@ __device__ __forceinline__ uint2 load8_masked(const uint8_t* row, int64_t off, i
   return make_uint2(v[0], v[1]);
 }
 
-// Same with byte loads only (scale rows of k/16 bytes need not be aligned).
-__device__ __forceinline__ uint2 load8_bytes(const uint8_t* row, int64_t off, int64_t valid) {
-  uint32_t v[2] = {0u, 0u};
-  for (int i = 0; i < 8; ++i)
-    if (off + i < valid) v[i >> 2] |= (uint32_t)row[off + i] << (8 * (i & 3));
-  return make_uint2(v[0], v[1]);
+__device__ __forceinline__ uint4 load16_codes(const uint8_t* row, int64_t off, int64_t rowb,
+                                              bool fast) {
+  if (fast) return *reinterpret_cast<const uint4*>(row + off);
+  uint2 lo = load8_masked(row, off, rowb), hi = load8_masked(row, off + 8, rowb);
+  return make_uint4(lo.x, lo.y, hi.x, hi.y);
 }
 
-template <int BM, int BN, bool FAST>
-__device__ __forceinline__ void load_stage(const GemmArgs& p, const TileRows<BM, BN>& tr,
-                                           const uint8_t* bq_base, const uint8_t* bsb_base,
-                                           int64_t k0, Stage<BM, BN, FAST>& st) {
-  const int tid = threadIdx.x;
-  const int64_t rowb = p.k / 2;    // code bytes per row
-  const int64_t rows_s = p.k / 16;  // scale bytes per row
-  const int part = tid & 3;         // which 16-byte chunk of the 64-byte stage row
-  const int64_t off = k0 / 2 + part * 16;
+__device__ __forceinline__ uint32_t pick(const uint4& v, int t) {
+  return (t & 3) == 0 ? v.x : (t & 3) == 1 ? v.y : (t & 3) == 2 ? v.z : v.w;
+}
+
+// ---------------------------------------------------------------------------
+// Register-direct variant: one wave per block, block tile = wave tile =
+// (32 TM) x (32 TN).  Each lane loads its own MFMA fragments straight from
+// global memory (L2) into a register double buffer one K stage ahead: lane
+// (li, h) reads, for every 32-row slab, 32 code bytes [32h, 32h + 32) of the
+// stage's 64 and the dword of 4 block scales covering them.  No LDS staging
+// and no barriers in the K loop; LDS only holds the per-row epilogue scales.
+template <int TM, int TN>
+struct RegStage {
+  uint4 a[TM][2];
+  uint4 b[TN][2];
+  uint32_t as[TM];
+  uint32_t bs[TN];
+};
+
+__device__ __forceinline__ uint32_t load4_bytes(const uint8_t* row, int64_t off, int64_t valid) {
+  uint32_t v = 0u;
+  for (int i = 0; i < 4; ++i)
+    if (off + i < valid) v |= (uint32_t)row[off + i] << (8 * i);
+  return v;
+}
+
+template <int TM, int TN, int VS, bool FAST>
+__device__ __forceinline__ void rd_load(const GemmArgs& p, const uint8_t* const* arow,
+                                        const uint8_t* const* asrow, const uint8_t* const* brow,
+                                        const uint8_t* const* bsrow, int h, int64_t k0,
+                                        RegStage<TM, TN>& r) {
+  const int64_t rowb = p.k / 2, rows_s = p.k / 16;
+  const int64_t off = k0 / 2 + 32 * h;
+  const int64_t soff = k0 / 16 + 4 * h;
 #pragma unroll
-  for (int i = 0; i < Stage<BM, BN, FAST>::ACH; ++i) {
-    const int64_t r = tr.arow[i];
-    if (r < 0) {
-      st.a[i] = make_uint4(0, 0, 0, 0);
+  for (int i = 0; i < VS; ++i) {
+    if (!arow[i]) {
+      r.a[i][0] = r.a[i][1] = make_uint4(0, 0, 0, 0);
+      r.as[i] = 0;
     } else if (FAST) {
-      st.a[i] = *reinterpret_cast<const uint4*>(p.a_q + r * rowb + off);
+      const uint4* q = reinterpret_cast<const uint4*>(arow[i] + off);
+      r.a[i][0] = q[0];
+      r.a[i][1] = q[1];
+      r.as[i] = *reinterpret_cast<const uint32_t*>(asrow[i] + soff);
     } else {
-      const uint8_t* rp = p.a_q + r * rowb;
-      uint2 lo = load8_masked(rp, off, rowb), hi = load8_masked(rp, off + 8, rowb);
-      st.a[i] = make_uint4(lo.x, lo.y, hi.x, hi.y);
+      r.a[i][0] = load16_codes(arow[i], off, rowb, false);
+      r.a[i][1] = load16_codes(arow[i], off + 16, rowb, false);
+      r.as[i] = load4_bytes(asrow[i], soff, rows_s);
     }
   }
 #pragma unroll
-  for (int i = 0; i < Stage<BM, BN, FAST>::BCH; ++i) {
-    const int64_t r = tr.brow[i];
-    if (r < 0) {
-      st.b[i] = make_uint4(0, 0, 0, 0);
+  for (int j = 0; j < TN; ++j) {
+    if (!brow[j]) {
+      r.b[j][0] = r.b[j][1] = make_uint4(0, 0, 0, 0);
+      r.bs[j] = 0;
     } else if (FAST) {
-      st.b[i] = *reinterpret_cast<const uint4*>(bq_base + r * rowb + off);
+      const uint4* q = reinterpret_cast<const uint4*>(brow[j] + off);
+      r.b[j][0] = q[0];
+      r.b[j][1] = q[1];
+      r.bs[j] = *reinterpret_cast<const uint32_t*>(bsrow[j] + soff);
     } else {
-      const uint8_t* rp = bq_base + r * rowb;
-      uint2 lo = load8_masked(rp, off, rowb), hi = load8_masked(rp, off + 8, rowb);
-      st.b[i] = make_uint4(lo.x, lo.y, hi.x, hi.y);
+      r.b[j][0] = load16_codes(brow[j], off, rowb, false);
+      r.b[j][1] = load16_codes(brow[j], off + 16, rowb, false);
+      r.bs[j] = load4_bytes(bsrow[j], soff, rows_s);
     }
-  }
-  const int64_t soff = k0 / 16;
-  if (tid < BM) {
-    if (tr.arow_s < 0) st.as = make_uint2(0, 0);
-    else if (FAST) st.as = *reinterpret_cast<const uint2*>(p.a_sb + tr.arow_s * rows_s + soff);
-    else st.as = load8_bytes(p.a_sb + tr.arow_s * rows_s, soff, rows_s);
-  }
-  if (tid < BN) {
-    if (tr.brow_s < 0) st.bs = make_uint2(0, 0);
-    else if (FAST) st.bs = *reinterpret_cast<const uint2*>(bsb_base + tr.brow_s * rows_s + soff);
-    else st.bs = load8_bytes(bsb_base + tr.brow_s * rows_s, soff, rows_s);
   }
 }
 
-template <int BM, int BN, bool FAST>
-__device__ __forceinline__ void store_stage(const Stage<BM, BN, FAST>& st, uint8_t* sA, uint8_t* sB,
-                                            uint8_t* sAs, uint8_t* sBs) {
-  const int tid = threadIdx.x;
-  const int part = tid & 3;
+template <int TM, int TN, int VS>
+__device__ __forceinline__ void rd_compute(const RegStage<TM, TN>& r, f32x16 (&acc)[TM][TN]) {
 #pragma unroll
-  for (int i = 0; i < Stage<BM, BN, FAST>::ACH; ++i) {
-    const int row = (tid + 256 * i) >> 2;
-    *reinterpret_cast<uint4*>(sA + row * SROW + part * 16) = st.a[i];
-  }
+  for (int t = 0; t < 8; ++t) {
+    f16x8 fa[TM], fb[TN];
 #pragma unroll
-  for (int i = 0; i < Stage<BM, BN, FAST>::BCH; ++i) {
-    const int row = (tid + 256 * i) >> 2;
-    *reinterpret_cast<uint4*>(sB + row * SROW + part * 16) = st.b[i];
+    for (int i = 0; i < VS; ++i) fa[i] = decode8(pick(r.a[i][t >> 2], t), scale_pair(r.as[i], t >> 1));
+#pragma unroll
+    for (int j = 0; j < TN; ++j) fb[j] = decode8(pick(r.b[j][t >> 2], t), scale_pair(r.bs[j], t >> 1));
+#pragma unroll
+    for (int i = 0; i < VS; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[i], fb[j], acc[i][j], 0, 0, 0);
   }
-  if (tid < BM) *reinterpret_cast<uint2*>(sAs + tid * SCB) = st.as;
-  if (tid < BN) *reinterpret_cast<uint2*>(sBs + tid * SCB) = st.bs;
+}
+
+template <int TM, int TN, int VS, bool FAST>
+__device__ __forceinline__ void rd_kloop(const GemmArgs& p, const uint8_t* const* arow,
+                                         const uint8_t* const* asrow, const uint8_t* const* brow,
+                                         const uint8_t* const* bsrow, int h,
+                                         f32x16 (&acc)[TM][TN]) {
+  const int64_t nstages = (p.k + BK - 1) / BK;
+  RegStage<TM, TN> r0, r1;
+  if (nstages > 0) rd_load<TM, TN, VS, FAST>(p, arow, asrow, brow, bsrow, h, 0, r0);
+  // two stages per iteration so the double buffer needs no register moves
+  int64_t s = 0;
+  for (; s + 1 < nstages; s += 2) {
+    rd_load<TM, TN, VS, FAST>(p, arow, asrow, brow, bsrow, h, (s + 1) * BK, r1);
+    rd_compute<TM, TN, VS>(r0, acc);
+    if (s + 2 < nstages) rd_load<TM, TN, VS, FAST>(p, arow, asrow, brow, bsrow, h, (s + 2) * BK, r0);
+    rd_compute<TM, TN, VS>(r1, acc);
+  }
+  if (s < nstages) rd_compute<TM, TN, VS>(r0, acc);
+}
+
+// Accumulate the tile over K with VS valid A slabs, then scale and store.
+template <int TM, int TN, int VS, bool FAST>
+__device__ __forceinline__ void rd_body(const GemmArgs& p, const uint8_t* const* arow,
+                                        const uint8_t* const* asrow, const uint8_t* const* brow,
+                                        const uint8_t* const* bsrow, int h, int li, int64_t row_lo,
+                                        int64_t row_hi, int64_t n0, const float* s_rowscale) {
+  f32x16 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < VS; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) acc[i][j] = (f32x16){0};
+  rd_kloop<TM, TN, VS, FAST>(p, arow, asrow, brow, bsrow, h, acc);
+  __syncthreads();  // s_rowscale (written by this wave) is visible
+#pragma unroll
+  for (int i = 0; i < VS; ++i) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int lrow = 32 * i + 8 * (r >> 2) + 4 * h + (r & 3);
+      const int64_t row = row_lo + lrow;
+      if (row >= row_hi) continue;
+      const float sc = s_rowscale[lrow];
+      float* yr = p.y + row * p.n;
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const int64_t col = n0 + 32 * j + li;
+        if (col < p.n) yr[col] = acc[i][j][r] * sc;
+      }
+    }
+  }
 }
 
 template <int TM, int TN, bool FAST>
-__global__ __launch_bounds__(256) void gemm_kernel(GemmArgs p) {
-  constexpr int WM = 32 * TM, WN = 32 * TN;
-  constexpr int BM = 2 * WM, BN = 2 * WN;
-  constexpr int A_BYTES = BM * SROW, B_BYTES = BN * SROW;
-  constexpr int STAGE_BYTES = A_BYTES + B_BYTES + (BM + BN) * SCB;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * STAGE_BYTES];
+__global__ __launch_bounds__(64) void gemm_rd_kernel(GemmArgs p) {
+  constexpr int BM = 32 * TM, BN = 32 * TN;
+  constexpr int GPT = MAX_GROUPS / 64;
   __shared__ int32_t s_prefix[MAX_GROUPS + 1];
-  __shared__ int32_t s_wsum[4];
+  __shared__ float s_rowscale[BM];
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int h = lane >> 5;   // K half of the stage this lane feeds
-  const int li = lane & 31;  // row (A) / column (B) inside a 32-slab
+  const int lane = threadIdx.x;
+  const int h = lane >> 5, li = lane & 31;
 
-  // ---- tile -> (group, rows, n0)
-  int64_t mt, row_lo, row_hi;
+  // ---- block -> XCD region -> tile.  Blocks are dealt round-robin to the
+  // 8 XCDs (block b runs on XCD b % 8); each XCD owns one region of an
+  // (8 / xcd_n) x xcd_n split of the tile grid so its L2 holds that region's
+  // A rows and B columns.  Inside a region, n runs fastest.
+  const int xcd = blockIdx.x % 8;
+  const int64_t jloc = blockIdx.x / 8;
+  const int xn = xcd % p.xcd_n, xm = xcd / p.xcd_n, XM = 8 / p.xcd_n;
+  const int64_t npx = (p.tiles_n + p.xcd_n - 1) / p.xcd_n;
+  const int64_t nlo = xn * npx, nhi = min((int64_t)p.tiles_n, nlo + npx);
+  if (nlo >= nhi) return;  // block-uniform
+  const int64_t nt = nlo + jloc % (nhi - nlo);
+  const int64_t mloc = jloc / (nhi - nlo);
+  int64_t mt;
+  int64_t row_lo, row_hi;
   int g = 0;
-  const int64_t tile = blockIdx.x;
-  const int64_t nt = tile % p.tiles_n;
-  mt = tile / p.tiles_n;
   if (p.offsets) {
-    // per-group m-tile counts and their exclusive prefix, from device offsets
     const int G = p.groups;
     int32_t local = 0;
-    int32_t cnt[MAX_GROUPS / 256];
+    int32_t cnt[GPT];
 #pragma unroll
-    for (int i = 0; i < MAX_GROUPS / 256; ++i) {
-      const int gg = tid * (MAX_GROUPS / 256) + i;
+    for (int i = 0; i < GPT; ++i) {
+      const int gg = lane * GPT + i;
       int32_t c = 0;
       if (gg < G) {
         int64_t lo = min(max((int64_t)p.offsets[gg], (int64_t)0), p.m_total);
@@ -223,28 +277,24 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs p) {
       cnt[i] = c;
       local += c;
     }
-    // block-wide exclusive scan of `local`
     int32_t incl = local;
 #pragma unroll
     for (int d = 1; d < 64; d <<= 1) {
       int32_t o = __shfl_up(incl, d, 64);
       if (lane >= d) incl += o;
     }
-    if (lane == 63) s_wsum[wave] = incl;
-    __syncthreads();
-    int32_t base = 0;
-    for (int w = 0; w < wave; ++w) base += s_wsum[w];
-    int32_t run = base + incl - local;
+    int32_t run = incl - local;
 #pragma unroll
-    for (int i = 0; i < MAX_GROUPS / 256; ++i) {
-      const int gg = tid * (MAX_GROUPS / 256) + i;
+    for (int i = 0; i < GPT; ++i) {
+      const int gg = lane * GPT + i;
       if (gg <= G) s_prefix[gg] = run;
       run += cnt[i];
     }
     __syncthreads();
-    const int32_t total_mt = s_prefix[G];
-    if (mt >= total_mt) return;  // block-uniform
-    // binary search: largest g with s_prefix[g] <= mt
+    const int64_t total_mt = s_prefix[G];
+    const int64_t mpx = (total_mt + XM - 1) / XM;
+    mt = xm * mpx + mloc;
+    if (mloc >= mpx || mt >= total_mt) return;  // block-uniform
     int lo = 0, hi = G - 1;
     while (lo < hi) {
       int mid = (lo + hi + 1) >> 1;
@@ -256,6 +306,10 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs p) {
     row_lo = glo + (mt - s_prefix[g]) * BM;
     row_hi = min(ghi, row_lo + BM);
   } else {
+    const int64_t tiles_m = (p.m_total + BM - 1) / BM;
+    const int64_t mpx = (tiles_m + XM - 1) / XM;
+    mt = xm * mpx + mloc;
+    if (mloc >= mpx || mt >= tiles_m) return;  // block-uniform
     row_lo = mt * BM;
     row_hi = min(p.m_total, row_lo + BM);
   }
@@ -269,122 +323,76 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs p) {
     return (r >= 0 && r < p.a_rows) ? r : -1;
   };
 
-  TileRows<BM, BN> tr;
-#pragma unroll
-  for (int i = 0; i < BM * 4 / 256; ++i) tr.arow[i] = a_source(row_lo + ((tid + 256 * i) >> 2));
-#pragma unroll
-  for (int i = 0; i < BN * 4 / 256; ++i) {
-    const int64_t c = n0 + ((tid + 256 * i) >> 2);
-    tr.brow[i] = c < p.n ? c : -1;
-  }
-  tr.arow_s = tid < BM ? a_source(row_lo + tid) : -1;
-  tr.brow_s = (tid < BN && n0 + tid < p.n) ? n0 + tid : -1;
-
-  f32x16 acc[TM][TN];
-#pragma unroll
-  for (int i = 0; i < TM; ++i)
-#pragma unroll
-    for (int j = 0; j < TN; ++j) acc[i][j] = (f32x16){0};
-
-  const int64_t nstages = (p.k + BK - 1) / BK;
-  Stage<BM, BN, FAST> st;
-  if (nstages > 0) {
-    load_stage<BM, BN, FAST>(p, tr, bq_base, bsb_base, 0, st);
-    uint8_t* s0 = smem;
-    store_stage<BM, BN, FAST>(st, s0, s0 + A_BYTES, s0 + A_BYTES + B_BYTES,
-                              s0 + A_BYTES + B_BYTES + BM * SCB);
-  }
-  __syncthreads();
-
-  for (int64_t s = 0; s < nstages; ++s) {
-    uint8_t* cur = smem + (s & 1) * STAGE_BYTES;
-    uint8_t* nxt = smem + ((s + 1) & 1) * STAGE_BYTES;
-    const bool more = s + 1 < nstages;
-    if (more) load_stage<BM, BN, FAST>(p, tr, bq_base, bsb_base, (s + 1) * BK, st);
-
-    const uint8_t* sA = cur;
-    const uint8_t* sB = cur + A_BYTES;
-    const uint8_t* sAs = cur + A_BYTES + B_BYTES;
-    const uint8_t* sBs = sAs + BM * SCB;
-    // this lane's 32 code bytes and 4 scale bytes per slab
-    uint4 ra[TM][2], rb[TN][2];
-    uint32_t sa4[TM], sb4[TN];
-#pragma unroll
-    for (int i = 0; i < TM; ++i) {
-      const int row = wm * WM + 32 * i + li;
-      const uint4* pa = reinterpret_cast<const uint4*>(sA + row * SROW + 32 * h);
-      ra[i][0] = pa[0];
-      ra[i][1] = pa[1];
-      sa4[i] = *reinterpret_cast<const uint32_t*>(sAs + row * SCB + 4 * h);
-    }
-#pragma unroll
-    for (int j = 0; j < TN; ++j) {
-      const int row = wn * WN + 32 * j + li;
-      const uint4* pb = reinterpret_cast<const uint4*>(sB + row * SROW + 32 * h);
-      rb[j][0] = pb[0];
-      rb[j][1] = pb[1];
-      sb4[j] = *reinterpret_cast<const uint32_t*>(sBs + row * SCB + 4 * h);
-    }
-#pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      f16x8 fa[TM], fb[TN];
-#pragma unroll
-      for (int i = 0; i < TM; ++i) {
-        const uint4& v = ra[i][t >> 2];
-        const uint32_t w = (t & 3) == 0 ? v.x : (t & 3) == 1 ? v.y : (t & 3) == 2 ? v.z : v.w;
-        fa[i] = decode8(w, scale_pair(sa4[i], t >> 1));
-      }
-#pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        const uint4& v = rb[j][t >> 2];
-        const uint32_t w = (t & 3) == 0 ? v.x : (t & 3) == 1 ? v.y : (t & 3) == 2 ? v.z : v.w;
-        fb[j] = decode8(w, scale_pair(sb4[j], t >> 1));
-      }
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[i], fb[j], acc[i][j], 0, 0, 0);
-    }
-    if (more)
-      store_stage<BM, BN, FAST>(st, nxt, nxt + A_BYTES, nxt + A_BYTES + B_BYTES,
-                                nxt + A_BYTES + B_BYTES + BM * SCB);
-    __syncthreads();
-  }
-
-  // ---- epilogue: Y = acc * (S_A[row] * S_B)
-  const float sbw = p.b_s[g];
+  const uint8_t* arow[TM];
+  const uint8_t* asrow[TM];
+  const uint8_t* brow[TN];
+  const uint8_t* bsrow[TN];
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
+    const int64_t r = a_source(row_lo + 32 * i + li);
+    arow[i] = r >= 0 ? p.a_q + r * (p.k / 2) : nullptr;
+    asrow[i] = r >= 0 ? p.a_sb + r * (p.k / 16) : nullptr;
+  }
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int64_t row = row_lo + wm * WM + 32 * i + 8 * (r >> 2) + 4 * h + (r & 3);
-      if (row >= row_hi) continue;
-      const int64_t ar = a_source(row);
-      const float sc = (ar >= 0 ? p.a_s[ar] : 0.0f) * sbw;
-      float* yr = p.y + row * p.n;
-#pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        const int64_t col = n0 + wn * WN + 32 * j + li;
-        if (col < p.n) yr[col] = acc[i][j][r] * sc;
-      }
+  for (int j = 0; j < TN; ++j) {
+    const int64_t c = n0 + 32 * j + li;
+    brow[j] = c < p.n ? bq_base + c * (p.k / 2) : nullptr;
+    bsrow[j] = c < p.n ? bsb_base + c * (p.k / 16) : nullptr;
+  }
+  {
+    const float sbw = p.b_s[g];
+    for (int r = lane; r < BM; r += 64) {
+      const int64_t ar = a_source(row_lo + r);
+      s_rowscale[r] = (ar >= 0 ? p.a_s[ar] : 0.0f) * sbw;
     }
+  }
+
+  // K loop and epilogue over the valid 32-row slabs only (ragged expert
+  // tiles skip the loads, decodes and MFMAs of empty slabs)
+  const int vslabs = (int)min((int64_t)TM, (row_hi - row_lo + 31) / 32);
+  static_assert(TM == 4, "slab dispatch is written for TM == 4");
+  switch (vslabs) {
+    case 4: rd_body<TM, TN, 4, FAST>(p, arow, asrow, brow, bsrow, h, li, row_lo, row_hi, n0, s_rowscale); break;
+    case 3: rd_body<TM, TN, 3, FAST>(p, arow, asrow, brow, bsrow, h, li, row_lo, row_hi, n0, s_rowscale); break;
+    case 2: rd_body<TM, TN, 2, FAST>(p, arow, asrow, brow, bsrow, h, li, row_lo, row_hi, n0, s_rowscale); break;
+    default: rd_body<TM, TN, 1, FAST>(p, arow, asrow, brow, bsrow, h, li, row_lo, row_hi, n0, s_rowscale); break;
   }
 }
 
+// Fill of an even split of `tiles` into `parts` ranges (1.0 = balanced).
+static double split_fill(int64_t tiles, int parts) {
+  const int64_t per = (tiles + parts - 1) / parts;
+  return per > 0 ? (double)tiles / (double)(per * parts) : 1.0;
+}
+
 template <int TM, int TN>
-static void launch_gemm(const GemmArgs& a, int64_t tiles_m, hipStream_t stream) {
-  constexpr int BN = 64 * TN;
+static void launch_gemm_rd(const GemmArgs& a, bool grouped, int64_t groups, hipStream_t stream) {
+  constexpr int BM = 32 * TM, BN = 32 * TN;
   GemmArgs p = a;
   p.tiles_n = (int)((p.n + BN - 1) / BN);
-  const int64_t blocks = tiles_m * p.tiles_n;
+  // upper bound on m-tiles (grouped: each group adds at most a partial tile;
+  // the exact count is derived on the device from the offsets)
+  const int64_t tiles_m = (p.m_total + BM - 1) / BM + (grouped ? groups : 0);
+  // XCD split: grouped GEMMs split along M (B changes along M); dense GEMMs
+  // take the split with the best balance, preferring more N regions.
+  p.xcd_n = 1;
+  if (!grouped) {
+    double best = -1.0;
+    for (int xn = 1; xn <= 8; xn *= 2) {
+      const double f = split_fill(tiles_m, 8 / xn) * split_fill(p.tiles_n, xn);
+      if (f >= best) { best = f; p.xcd_n = xn; }
+    }
+  }
+  const int64_t per_xcd = ((tiles_m + (8 / p.xcd_n) - 1) / (8 / p.xcd_n)) *
+                          ((p.tiles_n + p.xcd_n - 1) / p.xcd_n);
+  const int64_t blocks = 8 * per_xcd;
   const bool fast = (p.k % BK) == 0 && nvfp4host::aligned(p.a_q, 16) &&
-                    nvfp4host::aligned(p.b_q, 16) && nvfp4host::aligned(p.a_sb, 8) &&
-                    nvfp4host::aligned(p.b_sb, 8);
+                    nvfp4host::aligned(p.b_q, 16) && nvfp4host::aligned(p.a_sb, 4) &&
+                    nvfp4host::aligned(p.b_sb, 4);
   if (fast)
-    hipLaunchKernelGGL((gemm_kernel<TM, TN, true>), dim3((unsigned)blocks), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((gemm_rd_kernel<TM, TN, true>), dim3((unsigned)blocks), dim3(64), 0, stream, p);
   else
-    hipLaunchKernelGGL((gemm_kernel<TM, TN, false>), dim3((unsigned)blocks), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((gemm_rd_kernel<TM, TN, false>), dim3((unsigned)blocks), dim3(64), 0, stream, p);
 }
 
 // Y = 0 for k == 0 (no operand bytes to read).
@@ -392,9 +400,6 @@ __global__ __launch_bounds__(256) void zero_rows_kernel(float* __restrict__ y, i
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n_elems; i += (int64_t)gridDim.x * 256)
     y[i] = 0.0f;
 }
-
-constexpr int TM_DEF = 2, TN_DEF = 2;
-constexpr int BM_DEF = 64 * TM_DEF;
 
 }  // namespace nvfp4
 
@@ -424,8 +429,7 @@ extern "C" int nvfp4_gemm(const uint8_t* a_q, const uint8_t* a_sb, const float* 
   p.a_q = a_q; p.a_sb = a_sb; p.a_s = a_s; p.a_rows = m;
   p.row_index = nullptr; p.m_total = m; p.offsets = nullptr; p.groups = 1;
   p.b_q = b_q; p.b_sb = b_sb; p.b_s = b_s; p.n = n; p.k = k; p.y = y;
-  const int64_t tiles_m = (m + nvfp4::BM_DEF - 1) / nvfp4::BM_DEF;
-  nvfp4::launch_gemm<nvfp4::TM_DEF, nvfp4::TN_DEF>(p, tiles_m, str);
+  nvfp4::launch_gemm_rd<4, 4>(p, false, 1, str);
   return nvfp4host::launch_status();
 }
 
@@ -455,11 +459,8 @@ extern "C" int nvfp4_grouped_gemm(const uint8_t* a_q, const uint8_t* a_sb, const
   p.a_q = a_q; p.a_sb = a_sb; p.a_s = a_s; p.a_rows = a_rows;
   p.row_index = row_index; p.m_total = m_total; p.offsets = offsets; p.groups = (int)groups;
   p.b_q = b_q; p.b_sb = b_sb; p.b_s = b_s; p.n = n; p.k = k; p.y = y;
-  // upper bound on m-tiles without reading offsets: each group adds at most
-  // one partial tile
-  const int64_t tiles_m = (m_total + nvfp4::BM_DEF - 1) / nvfp4::BM_DEF + groups;
   // k == 0 needs no special case: the K loop is empty and the epilogue writes
   // zeros to exactly the rows the groups own
-  nvfp4::launch_gemm<nvfp4::TM_DEF, nvfp4::TN_DEF>(p, tiles_m, str);
+  nvfp4::launch_gemm_rd<4, 4>(p, true, groups, str);
   return nvfp4host::launch_status();
 }
