@@ -22,6 +22,19 @@ int check_arch() {
   return v == 1 ? NVFP4_SUCCESS : NVFP4_ERROR_ARCH;
 }
 
+int num_cus() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int v = __atomic_load_n(&cache[dev], __ATOMIC_ACQUIRE);
+  if (v == 0) {
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0)
+      v = 256;
+    __atomic_store_n(&cache[dev], v, __ATOMIC_RELEASE);
+  }
+  return v;
+}
+
 int launch_status() {
   return hipGetLastError() == hipSuccess ? NVFP4_SUCCESS : NVFP4_ERROR_LAUNCH;
 }

@@ -60,6 +60,7 @@ struct GemmArgs {
   float* y;
   int tiles_n;
   int xcd_n;  // XCD regions along N (8 / xcd_n along M), register-direct kernel
+  int slots;  // waves that run at once on one XCD (one per SIMD)
 };
 
 __device__ __forceinline__ f16x2 as_h2(uint32_t v) { return __builtin_bit_cast(f16x2, v); }
@@ -256,9 +257,28 @@ __global__ __launch_bounds__(64) void gemm_rd_kernel(GemmArgs p) {
   const int64_t npx = (p.tiles_n + p.xcd_n - 1) / p.xcd_n;
   const int64_t nlo = xn * npx, nhi = min((int64_t)p.tiles_n, nlo + npx);
   if (nlo >= nhi) return;  // block-uniform
-  const int64_t nt = nlo + jloc % (nhi - nlo);
-  const int64_t mloc = jloc / (nhi - nlo);
-  int64_t mt;
+  const int64_t width = nhi - nlo;
+  // Region tiles are issued in order; when the last round of a region would
+  // leave more than half of the XCD's wave slots idle, its tiles are issued
+  // as two 64-row halves so that round takes about half as long.
+  auto place = [&](int64_t mcount, int64_t& jf, int& hf) -> bool {
+    const int64_t T = mcount * width;
+    const int64_t tail = T % p.slots;
+    const int64_t split = (tail != 0 && 2 * tail <= p.slots) ? tail : 0;
+    const int64_t F = T - split;
+    if (jloc < F) {
+      jf = jloc;
+      hf = -1;
+      return true;
+    }
+    const int64_t hidx = jloc - F;
+    if (hidx >= 2 * split) return false;
+    jf = F + hidx / 2;
+    hf = (int)(hidx & 1);
+    return true;
+  };
+  int64_t jf = 0, mt, nt;
+  int hf = -1;
   int64_t row_lo, row_hi;
   int g = 0;
   if (p.offsets) {
@@ -293,8 +313,10 @@ __global__ __launch_bounds__(64) void gemm_rd_kernel(GemmArgs p) {
     __syncthreads();
     const int64_t total_mt = s_prefix[G];
     const int64_t mpx = (total_mt + XM - 1) / XM;
-    mt = xm * mpx + mloc;
-    if (mloc >= mpx || mt >= total_mt) return;  // block-uniform
+    const int64_t mcount = min(mpx, max(total_mt - xm * mpx, (int64_t)0));
+    if (!place(mcount, jf, hf)) return;  // block-uniform
+    mt = xm * mpx + jf / width;
+    nt = nlo + jf % width;
     int lo = 0, hi = G - 1;
     while (lo < hi) {
       int mid = (lo + hi + 1) >> 1;
@@ -308,10 +330,17 @@ __global__ __launch_bounds__(64) void gemm_rd_kernel(GemmArgs p) {
   } else {
     const int64_t tiles_m = (p.m_total + BM - 1) / BM;
     const int64_t mpx = (tiles_m + XM - 1) / XM;
-    mt = xm * mpx + mloc;
-    if (mloc >= mpx || mt >= tiles_m) return;  // block-uniform
+    const int64_t mcount = min(mpx, max(tiles_m - xm * mpx, (int64_t)0));
+    if (!place(mcount, jf, hf)) return;  // block-uniform
+    mt = xm * mpx + jf / width;
+    nt = nlo + jf % width;
     row_lo = mt * BM;
     row_hi = min(p.m_total, row_lo + BM);
+  }
+  if (hf >= 0) {  // half tile: rows [row_lo + 64 hf, row_lo + 64 hf + 64)
+    row_lo += 64 * hf;
+    row_hi = min(row_hi, row_lo + 64);
+    if (row_lo >= row_hi) return;  // block-uniform
   }
   const int64_t n0 = nt * BN;
   const uint8_t* bq_base = p.b_q + (int64_t)g * p.n * (p.k / 2);
@@ -383,8 +412,12 @@ static void launch_gemm_rd(const GemmArgs& a, bool grouped, int64_t groups, hipS
       if (f >= best) { best = f; p.xcd_n = xn; }
     }
   }
+  // one wave per SIMD (the kernel uses the whole register file)
+  p.slots = (nvfp4host::num_cus() / 8) * 4;
+  if (p.slots < 2) p.slots = 2;
   const int64_t per_xcd = ((tiles_m + (8 / p.xcd_n) - 1) / (8 / p.xcd_n)) *
-                          ((p.tiles_n + p.xcd_n - 1) / p.xcd_n);
+                              ((p.tiles_n + p.xcd_n - 1) / p.xcd_n) +
+                          p.slots / 2;  // room for the split tail
   const int64_t blocks = 8 * per_xcd;
   const bool fast = (p.k % BK) == 0 && nvfp4host::aligned(p.a_q, 16) &&
                     nvfp4host::aligned(p.b_q, 16) && nvfp4host::aligned(p.a_sb, 4) &&

@@ -82,6 +82,9 @@ inline bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0
 // Returns NVFP4_SUCCESS when the current device is gfx950 (cached per device).
 int check_arch();
 
+// Compute units of the current device (cached per device).
+int num_cus();
+
 // Maps the last HIP launch error to a status.
 int launch_status();
 

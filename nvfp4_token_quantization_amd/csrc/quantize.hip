@@ -26,6 +26,10 @@ namespace nvfp4 {
 
 enum QuantMode { MODE_ROW = 0, MODE_AMAX_IN = 1, MODE_GROUP = 2 };
 
+#ifndef NVFP4_Q_WAVES_PER_SIMD
+#define NVFP4_Q_WAVES_PER_SIMD 8
+#endif
+
 typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
@@ -94,40 +98,47 @@ __device__ __forceinline__ void block_scale(uint32_t amax_bits, float S, float t
   inv = (d != 0.0f) ? 1.0f / d : 0.0f;
 }
 
-// One row per L lanes; NB blocks per lane at most (nblk <= L * NB).
-template <int L, int NB, int MODE>
-__global__ __launch_bounds__(256) void quantize_rows_kernel(
-    const uint16_t* __restrict__ x, int64_t rows, int64_t k, int nblk,
-    const float* __restrict__ amax_src, int64_t rows_per_group, uint8_t* __restrict__ q,
-    uint8_t* __restrict__ sb, float* __restrict__ s) {
-  constexpr int RPW = 64 / L;
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int j = lane % L;
-  const int64_t row = ((int64_t)blockIdx.x * 4 + wave) * RPW + lane / L;
-  const bool row_ok = row < rows;
-
+// The NB blocks of one row group held by a lane (one 32-byte block is two
+// uint4 of bf16).
+template <int NB>
+struct RowData {
   uint4 d[NB][2];
+};
+
+template <int L, int NB>
+__device__ __forceinline__ void load_rows(const uint16_t* __restrict__ x, int64_t rows, int64_t k,
+                                          int nblk, int64_t row, int j, RowData<NB>& r) {
+  const bool row_ok = row < rows;
   const uint4* xr = reinterpret_cast<const uint4*>(x + (row_ok ? row : 0) * k);
 #pragma unroll
   for (int i = 0; i < NB; ++i) {
     const int b = j + L * i;
     if (row_ok && b < nblk) {
-      d[i][0] = ld_stream(xr + 2 * b);
-      d[i][1] = ld_stream(xr + 2 * b + 1);
+      r.d[i][0] = ld_stream(xr + 2 * b);
+      r.d[i][1] = ld_stream(xr + 2 * b + 1);
     } else {
-      d[i][0] = make_uint4(0, 0, 0, 0);
-      d[i][1] = make_uint4(0, 0, 0, 0);
+      r.d[i][0] = make_uint4(0, 0, 0, 0);
+      r.d[i][1] = make_uint4(0, 0, 0, 0);
     }
   }
+}
+
+// Encode and store one row group.  Must be called by all 64 lanes of the
+// wave (the row amax is a cross-lane reduction).
+template <int L, int NB, int MODE>
+__device__ __forceinline__ void encode_rows(const RowData<NB>& r, int64_t rows, int64_t k,
+                                            int nblk, int64_t row, int j,
+                                            const float* __restrict__ amax_src,
+                                            int64_t rows_per_group, uint8_t* __restrict__ q,
+                                            uint8_t* __restrict__ sb, float* __restrict__ s) {
+  const bool row_ok = row < rows;
   uint32_t bmax[NB];
   uint32_t rmax = 0;
 #pragma unroll
   for (int i = 0; i < NB; ++i) {
-    bmax[i] = block_amax_bits(d[i][0], d[i][1]);
+    bmax[i] = block_amax_bits(r.d[i][0], r.d[i][1]);
     rmax = max(rmax, bmax[i]);
   }
-
   float amax;
   if (MODE == MODE_ROW) {
     amax = __uint_as_float(group_max_u32<L>(rmax) << 16);
@@ -139,7 +150,6 @@ __global__ __launch_bounds__(256) void quantize_rows_kernel(
   const float S = amax / 2688.0f;
   if (MODE != MODE_GROUP && row_ok && j == 0) s[row] = S;
   const float t = 6.0f * S;
-
   uint8_t* qr = q + (row_ok ? row : 0) * (k / 2);
   uint8_t* sr = sb + (row_ok ? row : 0) * (k / 16);
 #pragma unroll
@@ -149,10 +159,39 @@ __global__ __launch_bounds__(256) void quantize_rows_kernel(
       uint32_t code;
       float inv;
       block_scale(bmax[i], S, t, code, inv);
-      uint2 packed = encode_block(d[i][0], d[i][1], inv);
-      reinterpret_cast<uint2*>(qr)[b] = packed;
+      reinterpret_cast<uint2*>(qr)[b] = encode_block(r.d[i][0], r.d[i][1], inv);
       sr[b] = (uint8_t)code;
     }
+  }
+}
+
+// One row per L lanes (NB blocks per lane at most, nblk <= L * NB); a wave
+// handles 64 / L rows per row group and walks row groups with a grid stride,
+// loading group i + 1 while it encodes group i (two register buffers,
+// unrolled by two so the buffers never move).
+template <int L, int NB, int MODE>
+__global__ __launch_bounds__(256) void quantize_rows_kernel(
+    const uint16_t* __restrict__ x, int64_t rows, int64_t k, int nblk,
+    const float* __restrict__ amax_src, int64_t rows_per_group, uint8_t* __restrict__ q,
+    uint8_t* __restrict__ sb, float* __restrict__ s) {
+  constexpr int RPW = 64 / L;
+  const int lane = threadIdx.x & 63;
+  const int j = lane % L;
+  const int sub = lane / L;
+  const int64_t ngroups = (rows + RPW - 1) / RPW;
+  const int64_t stride = (int64_t)gridDim.x * 4;
+  int64_t g0 = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);  // wave-uniform
+  RowData<NB> r0, r1;
+  if (g0 < ngroups) load_rows<L, NB>(x, rows, k, nblk, g0 * RPW + sub, j, r0);
+  for (; g0 < ngroups; g0 += 2 * stride) {
+    const int64_t g1 = g0 + stride, g2 = g1 + stride;
+    if (g1 < ngroups) load_rows<L, NB>(x, rows, k, nblk, g1 * RPW + sub, j, r1);
+    encode_rows<L, NB, MODE>(r0, rows, k, nblk, g0 * RPW + sub, j, amax_src, rows_per_group, q,
+                             sb, s);
+    if (g2 < ngroups) load_rows<L, NB>(x, rows, k, nblk, g2 * RPW + sub, j, r0);
+    if (g1 < ngroups)
+      encode_rows<L, NB, MODE>(r1, rows, k, nblk, g1 * RPW + sub, j, amax_src, rows_per_group,
+                               q, sb, s);
   }
 }
 
@@ -208,8 +247,9 @@ __global__ __launch_bounds__(256) void fill_zero_kernel(float* __restrict__ p, i
 }
 
 // Group amax: block (g, c) reduces chunk c of group g's contiguous elements
-// and folds it into amax[g] with an atomic max on the bit pattern (order
-// independent, so the result is deterministic).
+// (4 independent 16-byte streaming loads in flight per thread) and folds it
+// into amax[g] with an atomic max on the bit pattern (order independent, so
+// the result is deterministic).
 __global__ __launch_bounds__(256) void group_amax_kernel(const uint16_t* __restrict__ w,
                                                          int64_t group_elems, int64_t chunk_vecs,
                                                          int chunks, float* __restrict__ amax) {
@@ -222,12 +262,12 @@ __global__ __launch_bounds__(256) void group_amax_kernel(const uint16_t* __restr
   const int64_t v1 = min(nvec, v0 + chunk_vecs);
   uint32_t m = 0;
   int64_t v = v0 + threadIdx.x;
-  for (; v + 256 < v1; v += 512) {
-    uint4 a = ld_stream(base + v);
-    uint4 b = ld_stream(base + v + 256);
-    m = max(m, block_amax_bits(a, b));
+  for (; v + 3 * 256 < v1; v += 4 * 256) {
+    uint4 a = ld_stream(base + v), b = ld_stream(base + v + 256);
+    uint4 c2 = ld_stream(base + v + 512), d = ld_stream(base + v + 768);
+    m = max(m, max(block_amax_bits(a, b), block_amax_bits(c2, d)));
   }
-  if (v < v1) m = max(m, block_amax_bits(base[v], make_uint4(0, 0, 0, 0)));
+  for (; v < v1; v += 256) m = max(m, block_amax_bits(base[v], make_uint4(0, 0, 0, 0)));
   m = group_max_u32<64>(m);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
   __syncthreads();
@@ -287,8 +327,12 @@ static void launch_rows(const uint16_t* x, int64_t rows, int64_t k, const float*
   int lanes = 0;
   RowKernel kern = pick_row_kernel<MODE>(nblk, lanes);
   if (kern) {
+    // enough resident waves to keep HBM busy, and several row groups per wave
+    // so loads overlap encoding (NVFP4_Q_WAVES_PER_SIMD waves per SIMD)
     const int64_t rows_per_block = 4 * (64 / lanes);
-    dim3 grid((unsigned)((rows + rows_per_block - 1) / rows_per_block));
+    const int64_t need = (rows + rows_per_block - 1) / rows_per_block;
+    const int64_t cap = (int64_t)nvfp4host::num_cus() * NVFP4_Q_WAVES_PER_SIMD;
+    dim3 grid((unsigned)(need < cap ? need : cap));
     hipLaunchKernelGGL(kern, grid, dim3(256), 0, stream, x, rows, k, nblk, amax_src,
                        rows_per_group, q, sb, s);
   } else {
@@ -355,9 +399,11 @@ extern "C" int nvfp4_quantize_weight(const uint16_t* w_bf16, int64_t groups, int
                        amax_out, groups);
     const int64_t group_elems = rows_per_group * k;
     if (group_elems > 0) {
-      // about 64 KiB of bf16 per block
+      // large chunks (up to 1 MiB of bf16 per block) keep the reads streaming;
+      // at least ~1024 blocks keep every CU busy
       const int64_t nvec = group_elems / 8;
-      int64_t chunk_vecs = 4096;
+      int64_t chunk_vecs = (nvec * groups) / 1024;
+      chunk_vecs = chunk_vecs < 4096 ? 4096 : (chunk_vecs > 65536 ? 65536 : chunk_vecs);
       int64_t chunks = (nvec + chunk_vecs - 1) / chunk_vecs;
       if (chunks * groups > ((int64_t)1 << 30)) return NVFP4_ERROR_UNSUPPORTED_SHAPE;
       hipLaunchKernelGGL(nvfp4::group_amax_kernel, dim3((unsigned)(chunks * groups)), dim3(256), 0,
