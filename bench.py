@@ -22,6 +22,13 @@ or flops (stated in the design notes) over that duration.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
 Prints one JSON line on stdout; progress goes to stderr.
+
+Traffic counters (profiles/traffic.json, used for roofline.traffic):
+  rocprofv3 --pmc FETCH_SIZE (then WRITE_SIZE) --output-format csv -d DIR -- \
+      python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline
+  the same two counters over `python3 bench.py --calib-copy` (a plain 1 GiB
+  device copy), then
+  python bench.py --pmc-summary FETCH_DIR WRITE_DIR CALIB_FETCH_DIR CALIB_WRITE_DIR
 """
 import argparse
 import hashlib
@@ -70,14 +77,95 @@ def gemm_bytes(a_rows, m_out, n, k, groups):
     return a + b + m_out * n * 4
 
 
+# Launch order of one step and the number of kernel dispatches each makes
+# (a weight quantize is: clear amax target, group amax, outer scales, encode).
+STEP_LAUNCHES = [("quantize_weight_dense", 4), ("quantize_weight_up", 4),
+                 ("quantize_weight_down", 4), ("quantize_rows_dense", 1), ("quantize_rows_moe", 1),
+                 ("gemm_dense", 1), ("grouped_gemm_up", 1), ("requantize_rows_amax_reuse", 1),
+                 ("grouped_gemm_down", 1)]
+CALIB_BYTES = 1 << 30
+
+
+def calib_copy():
+    """Plain device copy of CALIB_BYTES (the FETCH_SIZE / WRITE_SIZE
+    calibration workload: reads and writes exactly that many bytes)."""
+    import torch
+    dev = torch.device("cuda:0")
+    src = torch.ones(CALIB_BYTES // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calib_copy_bytes": CALIB_BYTES}))
+
+
+def _pmc_dispatches(csv_dir, counter):
+    """(dispatch id, kernel name, grid, value) rows of one rocprofv3 --pmc
+    csv output, value summed over counter instances."""
+    import csv
+    import glob
+    files = glob.glob(os.path.join(csv_dir, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit("no counter_collection.csv under %s" % csv_dir)
+    acc = {}
+    for f in files:
+        for r in csv.DictReader(open(f)):
+            if r["Counter_Name"] != counter:
+                continue
+            key = int(r["Dispatch_Id"])
+            d = acc.setdefault(key, [r["Kernel_Name"], int(r["Grid_Size"]), 0.0])
+            d[2] += float(r["Counter_Value"])
+    return [(k, v[0], v[1], v[2]) for k, v in sorted(acc.items())]
+
+
+def pmc_summary(fetch_dir, write_dir, cfetch_dir, cwrite_dir):
+    """Per-launch HBM bytes of every step launch from FETCH_SIZE and
+    WRITE_SIZE runs of this bench, each scaled by the same counter's reading
+    for a plain copy of CALIB_BYTES; writes profiles/traffic.json."""
+    out = {"csrc_digest": csrc_digest(), "calibration": {}, "kernels": {}}
+    per = {}
+    for counter, ddir, cdir in (("FETCH_SIZE", fetch_dir, cfetch_dir),
+                                ("WRITE_SIZE", write_dir, cwrite_dir)):
+        cal = [d for d in _pmc_dispatches(cdir, counter) if "nvfp4" not in d[1]]
+        big = max(cal, key=lambda d: d[3])
+        factor = (CALIB_BYTES / 1024.0) / big[3]
+        out["calibration"][counter] = {"copy_kernel": big[1], "copy_bytes": CALIB_BYTES,
+                                       "counter_KiB": big[3], "factor": factor}
+        disp = [d for d in _pmc_dispatches(ddir, counter) if "nvfp4" in d[1]]
+        n_per_step = sum(c for _, c in STEP_LAUNCHES)
+        steps = len(disp) // n_per_step
+        if steps * n_per_step != len(disp):
+            raise SystemExit("%s: %d nvfp4 dispatches is not a whole number of steps" %
+                             (counter, len(disp)))
+        for st in range(steps):
+            i = st * n_per_step
+            for name, cnt in STEP_LAUNCHES:
+                kib = sum(d[3] for d in disp[i:i + cnt])
+                per.setdefault(name, {}).setdefault(counter, []).append(kib * 1024.0 * factor)
+                i += cnt
+    for name, d in per.items():
+        f = sum(d["FETCH_SIZE"]) / len(d["FETCH_SIZE"])
+        w = sum(d["WRITE_SIZE"]) / len(d["WRITE_SIZE"])
+        out["kernels"][name] = {"fetch_bytes": round(f), "write_bytes": round(w),
+                                "bytes_per_launch": round(f + w)}
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    json.dump(out, open(path, "w"), indent=1)
+    print(json.dumps(out, indent=1))
+
+
 def main():
+    if len(sys.argv) > 1 and sys.argv[1] == "--calib-copy":
+        return calib_copy()
+    if len(sys.argv) > 1 and sys.argv[1] == "--pmc-summary":
+        return pmc_summary(*sys.argv[2:6])
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-rows", type=int, default=4096)
-    ap.add_argument("--cpu-sample-entries", type=int, default=8000000)
+    ap.add_argument("--cpu-sample-entries", type=int, default=30000000)
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
