@@ -155,9 +155,9 @@ int nvfp4_gemm(const uint8_t* a_q, const uint8_t* a_sb, const float* a_s, int64_
  *             [0, m_total]; rows at or past offsets[groups] are not written.
  *   B: b_q [groups, n, k/2], b_sb [groups, n, k/16], b_s [groups] (per expert)
  *   y  [m_total, n] f32 out
- * Accuracy as nvfp4_gemm.  groups <= 4096.
+ * Accuracy as nvfp4_gemm.  groups <= 1024.
  * Errors: INVALID_VALUE (groups < 1, negative sizes, null pointers),
- * UNSUPPORTED_SHAPE (k % 16 != 0, groups > 4096), MISALIGNED, ARCH, LAUNCH.
+ * UNSUPPORTED_SHAPE (k % 16 != 0, groups > 1024), MISALIGNED, ARCH, LAUNCH.
  */
 int nvfp4_grouped_gemm(const uint8_t* a_q, const uint8_t* a_sb, const float* a_s, int64_t a_rows,
                        const int32_t* row_index, int64_t m_total, const int32_t* offsets,

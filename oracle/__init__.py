@@ -68,6 +68,9 @@ def lib():
         L.oracle_quantize_weight.argtypes = [P, I64, I64, I64, P, P, P, P, P]
         L.oracle_quantize_weight.restype = ctypes.c_int
         L.oracle_dequantize.argtypes = [P, P, P, P, I64, I64, P]
+        L.oracle_f32_to_bf16_array.argtypes = [P, I64, P]
+        L.oracle_swiglu_rows.argtypes = [P, I64, I64, P]
+        L.oracle_swiglu_rows.restype = ctypes.c_int
         L.oracle_gemm_entries.argtypes = [P, P, P, P, P, P, I64, P, P, P, I64, P, P]
         L.oracle_gemm.argtypes = [P, P, P, I64, P, P, P, I64, I64, P, P]
         L.oracle_grouped_gemm.argtypes = [P, P, P, P, P, I64, P, P, P, I64, I64, P, P]
@@ -171,6 +174,40 @@ def dequantize(q, sb, s, s_index=None):
     out = np.empty((rows, k), np.float64)
     lib().oracle_dequantize(_p(q), _p(sb), _p(s), _p(si), rows, k, _p(out))
     return out
+
+
+# ------------------------------------------------------------ bf16, SwiGLU --
+def f32_to_bf16(v):
+    """bf16 bit patterns nearest to fp32 values (ties to even; not NaN)."""
+    v = _c(v, np.float32)
+    out = np.empty(v.shape, np.uint16)
+    lib().oracle_f32_to_bf16_array(_p(v), v.size, _p(out))
+    return out
+
+
+def swiglu_rows(gate_up):
+    """h = bf16(fl32(silu(g) * u)) for a fused fp32 [rows, 2f] gate|up block
+    (gate in columns [0, f), up in [f, 2f)).  Returns uint16 bf16 [rows, f]."""
+    gu = _c(gate_up, np.float32)
+    rows, f2 = gu.shape
+    if f2 % 2:
+        raise ValueError("gate_up must have an even number of columns")
+    f = f2 // 2
+    h = np.empty((rows, f), np.uint16)
+    if lib().oracle_swiglu_rows(_p(gu), rows, f, _p(h)) != 0:
+        raise ValueError("oracle_swiglu_rows: non-finite input or result")
+    return h
+
+
+def swiglu_quantize_rows(gate_up):
+    """The fused SwiGLU -> per-token quantize chain: H = swiglu_rows(gate_up),
+    its exact row amax, and quantize_rows(H) (which equals quantize_rows(H,
+    amax_in=amax): amax reuse).  Returns (h, amax, q, sb, s)."""
+    h = swiglu_rows(gate_up)
+    amax = (np.abs((h.astype(np.uint32) << 16).view(np.float32)).max(axis=1)
+            if h.shape[1] else np.zeros((h.shape[0],), np.float32)).astype(np.float32)
+    q, sb, s = quantize_rows(h)
+    return h, amax, q, sb, s
 
 
 # -------------------------------------------------------------------- GEMM --

@@ -232,6 +232,65 @@ void oracle_dequantize(const uint8_t* q, const uint8_t* sb, const float* s,
     }
 }
 
+/* ---------------------------------------------------------------- bf16 -- */
+
+/* bf16 bit pattern nearest to the fp32 value v (IEEE round to nearest, ties to
+ * the even pattern).  Truncating v's low 16 bits gives the neighbour on the
+ * zero side; the pattern one above it is the neighbour away from zero (past
+ * the largest finite bf16 that neighbour is infinity, which rounding treats as
+ * the value 2^128, so halfway and beyond overflow as IEEE requires).  v must
+ * not be NaN. */
+static uint16_t f32_to_bf16_nearest(float v) {
+    uint32_t u;
+    memcpy(&u, &v, 4);
+    uint16_t lo = (uint16_t)(u >> 16);
+    if ((u & 0xFFFFu) == 0) return lo;
+    uint16_t hi = (uint16_t)(lo + 1);
+    double lv = bf16_to_f32(lo);
+    double hv = ((hi & 0x7FFF) == 0x7F80) ? copysign(ldexp(1.0, 128), v) : bf16_to_f32(hi);
+    double dl = fabs((double)v - lv), dh = fabs(hv - (double)v);
+    if (dl < dh) return lo;
+    if (dh < dl) return hi;
+    return (lo & 1) ? hi : lo;
+}
+
+void oracle_f32_to_bf16_array(const float* v, int64_t n, uint16_t* out) {
+    #pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; ++i) out[i] = f32_to_bf16_nearest(v[i]);
+}
+
+/* -------------------------------------------------------------- SwiGLU -- */
+
+/* SwiGLU over a fused gate|up row block (the pages' MoE layers fuse the gate
+ * and up projections into one GEMM sharing one FP32 weight scale: Miles page,
+ * section 并行度与张量转换的一致性契约; SwiGLU itself is silu(gate) * up, with
+ * silu(g) = g * sigmoid(g) = g / (1 + e^-g), Shazeer, "GLU Variants Improve
+ * Transformer", 2020).
+ *
+ * gate_up is fp32 [rows, 2f]: columns [0, f) hold the gate projection and
+ * [f, 2f) the up projection of the same token.  Output h is bf16 [rows, f]:
+ * h = bf16(fl32(silu(g) * u)), the real value evaluated in fp64 as
+ * (g * u) / (1 + exp(-g)) (g * u is exact in fp64), rounded once to fp32 and
+ * then to bf16, both to nearest even.  Returns -1 on a bad shape, a
+ * non-finite input or a result that is not finite in fp32, else 0. */
+int oracle_swiglu_rows(const float* gate_up, int64_t rows, int64_t f, uint16_t* h) {
+    if (rows < 0 || f < 0) return -1;
+    int bad = 0;
+    #pragma omp parallel for schedule(static) reduction(| : bad)
+    for (int64_t r = 0; r < rows; ++r) {
+        const float* gr = gate_up + r * 2 * f;
+        for (int64_t j = 0; j < f; ++j) {
+            double g = gr[j], u = gr[f + j];
+            if (!isfinite(g) || !isfinite(u)) { bad = 1; h[r * f + j] = 0; continue; }
+            double hv = (g * u) / (1.0 + exp(-g));
+            float h32 = (float)hv;
+            if (!isfinite(h32)) { bad = 1; h[r * f + j] = 0; continue; }
+            h[r * f + j] = f32_to_bf16_nearest(h32);
+        }
+    }
+    return bad ? -1 : 0;
+}
+
 /* ------------------------------------------------------------------ GEMM -- */
 
 /* s_b * e2m1(code) * 2^10 as an exact integer, tabulated once per call for
