@@ -339,6 +339,35 @@ def main():
                         "frac_mfma": round(ach / MFMA_F16_PEAK_TFS, 4), "flop": amount,
                         "GB/s_algorithmic": round(gemm_traffic[n] / t / 1e9, 1)}
 
+    # rows of the pages' "next" list, timed on their own after the step (not
+    # part of `value`): each launched back to back K times between two events
+    nxt = {}
+
+    def time_extra(fn, iters):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        fn()
+        torch.cuda.synchronize()
+        a.record(stream)
+        for _ in range(iters):
+            st = fn()
+            if st != 0:
+                raise RuntimeError("extra launch failed: %s" % nv.status_string(st))
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / iters
+
+    # SwiGLU -> per-token requantize chained on the step's own up-GEMM output
+    # (fused gate|up, 32768 x 1536 fp32 -> H 32768 x 768 quantized in place)
+    FH = N3 // 2
+    sw = (empty((MR, FH // 2), u8), empty((MR, FH // 16), u8), empty((MR,), f32), empty((MR,), f32))
+    ms = time_extra(lambda: L.nvfp4_swiglu_quantize_rows(
+        p(out["y3"]), MR, FH, None, p(sw[3]), p(sw[0]), p(sw[1]), p(sw[2]), sp), K)
+    byt = MR * N3 * 4 + MR * FH // 2 + MR * FH // 16 + 2 * MR * 4
+    nxt["swiglu_quantize_chained"] = {"ms": round(ms, 4), "GB/s": round(byt / ms / 1e6, 1),
+                                      "frac_hbm": round(byt / ms / 1e6 / HBM_PEAK_GBS, 4),
+                                      "bytes": int(byt)}
+    log("next rows: %s" % nxt)
+
     # dominant kernel = longest per step
     dom = max(names, key=lambda n: per_kernel_ms[n])
     kind, amount = work[dom]
@@ -396,6 +425,7 @@ def main():
             "grouped_gemm_up_frac_mfma": comps["grouped_gemm_up"]["frac_mfma"],
         },
         "components": comps,
+        "next_rows": nxt,
         "roofline": roof,
         "cpu_baseline": None,
     }

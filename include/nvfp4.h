@@ -115,6 +115,34 @@ int nvfp4_quantize_weight(const uint16_t* w_bf16, int64_t groups, int64_t rows_p
                           uint8_t* sb, float* s, void* stream);
 
 /*
+ * SwiGLU of a fused gate|up projection, fused with per-token NVFP4
+ * quantization of its bf16 output (the row amax never leaves the kernel).
+ *
+ * Defined by: the miniTE page, section Transformer Engine路径优化 (amax reuse
+ * and fusion around the grouped GEMMs), and the Miles page, section
+ * 并行度与张量转换的一致性契约 (the MoE layers' gate and up projections are one
+ * fused GEMM); SwiGLU is silu(gate) * up with silu(g) = g / (1 + e^-g).
+ *
+ *   gate_up  [rows, 2f] f32: columns [0, f) gate, [f, 2f) up of one token
+ *            (the output of a GEMM against the fused [2f, K] weight).
+ *            f % 16 == 0, f <= 12288.  Values and results must be finite.
+ *   h_out    NULL or [rows, f] bf16 bits out: h = bf16(fl32(g * u / (1 +
+ *            exp(-g)))), the quotient formed in fp64, both roundings to
+ *            nearest even.
+ *   amax_out NULL or [rows] f32 out: max_j |h[r, j]| (the amax to reuse).
+ *   q, sb, s all NULL (produce only h and/or amax), or all given (q and sb
+ *            may be NULL when f == 0): the quantization of h, bit-identical to nvfp4_quantize_rows(h, rows,
+ *            f, amax_in = NULL or amax_out, q, sb, s).
+ * At least one output is required.  Each row depends only on its own row.
+ * Errors: INVALID_VALUE (negative sizes, a partial q/sb/s set, no output,
+ * null gate_up with work), UNSUPPORTED_SHAPE (f % 16 != 0, f > 12288),
+ * MISALIGNED (gate_up, h_out, q need 16 bytes; s, amax_out 4), ARCH, LAUNCH.
+ */
+int nvfp4_swiglu_quantize_rows(const float* gate_up, int64_t rows, int64_t f, uint16_t* h_out,
+                               float* amax_out, uint8_t* q, uint8_t* sb, float* s,
+                               void* stream);
+
+/*
  * Dense block-scaled W4A4 GEMM: Y = deq(A) . deq(B)^T with the per-token
  * scale and the weight scale applied in the epilogue, Y = S_A[m] * S_B *
  * sum_k (s_bA q_A)(s_bB q_B).

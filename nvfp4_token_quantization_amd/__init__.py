@@ -53,9 +53,11 @@ def lib():
         L.nvfp4_quantize_weight.argtypes = [P, I64, I64, I64, P, P, P, P, P, P]
         L.nvfp4_gemm.argtypes = [P, P, P, I64, P, P, P, I64, I64, P, P]
         L.nvfp4_grouped_gemm.argtypes = [P, P, P, I64, P, I64, P, I64, P, P, P, I64, I64, P, P]
+        L.nvfp4_swiglu_quantize_rows.argtypes = [P, I64, I64, P, P, P, P, P, P]
         L.nvfp4_debug_encode_e2m1.argtypes = [P, I64, P, P]
         L.nvfp4_debug_encode_e4m3.argtypes = [P, I64, P, P]
         for f in ("nvfp4_quantize_rows", "nvfp4_quantize_weight", "nvfp4_gemm",
+                  "nvfp4_swiglu_quantize_rows",
                   "nvfp4_grouped_gemm", "nvfp4_debug_encode_e2m1", "nvfp4_debug_encode_e4m3"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
@@ -123,6 +125,43 @@ def nvfp4_quantize_rows(x, amax_in=None, out=None):
                                    _stream(dev))
     _check("nvfp4_quantize_rows", st)
     return q, sb, s
+
+
+def nvfp4_swiglu_quantize_rows(gate_up, want_h=False, want_amax=False, quantize=True, out=None):
+    """SwiGLU of a fused fp32 gate|up block [rows, 2f] (gate in columns
+    [0, f), up in [f, 2f)) fused with per-token NVFP4 of its bf16 output.
+
+    Returns a dict with the requested outputs: "h" (bf16 [rows, f]), "amax"
+    (float32 [rows]) and "q", "sb", "s" when quantize is true.  `out` may hold
+    preallocated tensors under the same keys.
+    """
+    _dev(gate_up, "gate_up", (torch.float32,), 2)
+    rows, f2 = gate_up.shape
+    if f2 % 2:
+        raise ValueError("gate_up must have an even number of columns")
+    f = f2 // 2
+    dev = gate_up.device
+    out = dict(out or {})
+    res = {}
+    if want_h:
+        res["h"] = out.get("h", None)
+        if res["h"] is None:
+            res["h"] = torch.empty((rows, f), dtype=torch.bfloat16, device=dev)
+    if want_amax:
+        res["amax"] = out.get("amax", None)
+        if res["amax"] is None:
+            res["amax"] = torch.empty((rows,), dtype=torch.float32, device=dev)
+    if quantize:
+        for key, shape, dt in (("q", (rows, f // 2), torch.uint8), ("sb", (rows, f // 16), torch.uint8),
+                               ("s", (rows,), torch.float32)):
+            res[key] = out.get(key, None)
+            if res[key] is None:
+                res[key] = torch.empty(shape, dtype=dt, device=dev)
+    st = lib().nvfp4_swiglu_quantize_rows(_ptr(gate_up), rows, f, _ptr(res.get("h")),
+                                          _ptr(res.get("amax")), _ptr(res.get("q")),
+                                          _ptr(res.get("sb")), _ptr(res.get("s")), _stream(dev))
+    _check("nvfp4_swiglu_quantize_rows", st)
+    return res
 
 
 def nvfp4_quantize_weight(w, amax_in=None, out=None):

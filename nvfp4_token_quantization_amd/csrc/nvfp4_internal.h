@@ -36,6 +36,16 @@ __device__ __forceinline__ float e4m3_decode(uint32_t c) {
   return e ? nrm : sub;
 }
 
+// Block scale code and reciprocal of d = S * s_b for one block whose largest
+// magnitude has the bf16 bit pattern amax_bits (t = 6 * S).
+__device__ __forceinline__ void block_scale(uint32_t amax_bits, float S, float t, uint32_t& code,
+                                            float& inv) {
+  float ab = __uint_as_float(amax_bits << 16);
+  code = (S == 0.0f) ? 0u : e4m3_encode(ab / t);
+  float d = S * e4m3_decode(code);
+  inv = (d != 0.0f) ? 1.0f / d : 0.0f;
+}
+
 // ------------------------------------------------------------ E2M1 codec --
 // Two fp32 values -> two E2M1 codes in byte `sel` of `old` (src0 in the low
 // nibble).  gfx950's converter with scale 1.0 rounds to nearest even with

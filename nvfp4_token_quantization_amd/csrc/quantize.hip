@@ -89,15 +89,6 @@ __device__ __forceinline__ uint2 encode_block(const uint4& a, const uint4& b, fl
   return make_uint2(q0, q1);
 }
 
-// Block scale code and reciprocal of d = S * s_b for one block.
-__device__ __forceinline__ void block_scale(uint32_t amax_bits, float S, float t, uint32_t& code,
-                                            float& inv) {
-  float ab = __uint_as_float(amax_bits << 16);
-  code = (S == 0.0f) ? 0u : e4m3_encode(ab / t);
-  float d = S * e4m3_decode(code);
-  inv = (d != 0.0f) ? 1.0f / d : 0.0f;
-}
-
 // The NB blocks of one row group held by a lane (one 32-byte block is two
 // uint4 of bf16).
 template <int NB>

@@ -106,6 +106,22 @@ def test_grouped_gemm_argument_errors(L):
     assert f(None, None, None, 0, None, 0, None, 2, None, None, None, 8, 16, None, None) == OK
 
 
+def test_swiglu_quantize_argument_errors(L):
+    f = L.nvfp4_swiglu_quantize_rows
+    a = P(FAKE)
+    assert f(a, -1, 16, None, None, a, a, a, None) == INVALID
+    assert f(a, 4, 24, None, None, a, a, a, None) == SHAPE            # f % 16
+    assert f(a, 4, 12304, None, None, a, a, a, None) == SHAPE         # f > 12288
+    assert f(a, 4, 16, None, None, None, None, None, None) == INVALID  # no output
+    assert f(a, 4, 16, None, None, a, None, a, None) == INVALID       # partial q/sb/s
+    assert f(a, 4, 16, None, None, a, a, None, None) == INVALID       # q, sb without s
+    assert f(None, 4, 16, None, None, a, a, a, None) == INVALID
+    assert f(P(FAKE + 4), 4, 16, None, None, a, a, a, None) == MISALIGNED
+    assert f(a, 4, 16, P(FAKE + 8), None, a, a, a, None) == MISALIGNED
+    assert f(a, 4, 16, None, P(FAKE + 2), None, None, None, None) == MISALIGNED
+    assert f(None, 0, 16, None, None, None, None, None, None) == OK     # no rows: nothing to do
+
+
 def test_debug_hooks_argument_errors(L):
     assert L.nvfp4_debug_encode_e2m1(None, 4, P(FAKE), None) == INVALID
     assert L.nvfp4_debug_encode_e4m3(P(FAKE), -1, P(FAKE), None) == INVALID
