@@ -71,6 +71,8 @@ def lib():
         L.oracle_f32_to_bf16_array.argtypes = [P, I64, P]
         L.oracle_swiglu_rows.argtypes = [P, I64, I64, P]
         L.oracle_swiglu_rows.restype = ctypes.c_int
+        L.oracle_route.argtypes = [P, I64, I64, I64, P, P, P, P]
+        L.oracle_route.restype = ctypes.c_int
         L.oracle_gemm_entries.argtypes = [P, P, P, P, P, P, I64, P, P, P, I64, P, P]
         L.oracle_gemm.argtypes = [P, P, P, I64, P, P, P, I64, I64, P, P]
         L.oracle_grouped_gemm.argtypes = [P, P, P, P, P, I64, P, P, P, I64, I64, P, P]
@@ -208,6 +210,26 @@ def swiglu_quantize_rows(gate_up):
             if h.shape[1] else np.zeros((h.shape[0],), np.float32)).astype(np.float32)
     q, sb, s = quantize_rows(h)
     return h, amax, q, sb, s
+
+
+# ----------------------------------------------------------------- routing --
+def route(logits, topk=8):
+    """Top-k routing of fp32 logits [T, E] into the contiguous per-expert
+    layout.  Returns dict(experts int32 [T, topk] (descending logit, lower id
+    first on ties), offsets int32 [E+1], row_index int32 [T*topk] (token of
+    each routed row, ordered by expert then token), slot_of int32 [T, topk]
+    (routed row of each choice), counts int64 [E])."""
+    lg = _c(logits, np.float32)
+    T, E = lg.shape
+    experts = np.empty((T, topk), np.int32)
+    offsets = np.empty((E + 1,), np.int32)
+    row_index = np.empty((T * topk,), np.int32)
+    slot_of = np.empty((T, topk), np.int32)
+    if lib().oracle_route(_p(lg), T, E, topk, _p(experts), _p(offsets), _p(row_index),
+                          _p(slot_of)) != 0:
+        raise ValueError("oracle_route: bad shape or non-finite logit")
+    return dict(experts=experts, offsets=offsets, row_index=row_index, slot_of=slot_of,
+                counts=np.diff(offsets).astype(np.int64))
 
 
 # -------------------------------------------------------------------- GEMM --

@@ -291,6 +291,58 @@ int oracle_swiglu_rows(const float* gate_up, int64_t rows, int64_t f, uint16_t* 
     return bad ? -1 : 0;
 }
 
+/* -------------------------------------------------------------- routing -- */
+
+/* Top-k MoE routing into the contiguous per-expert layout (miniTE page,
+ * section Transformer Engine路径优化: contiguous layouts and device-side
+ * metadata for the grouped GEMMs; the layers route each token to its top-k
+ * experts by router logit, softmax being monotone).
+ *
+ * logits fp32 [T, E], finite.  For token t, experts[t, j] (j < topk) is the
+ * expert with the j-th largest logit; equal logits rank the lower expert id
+ * first (+0 and -0 are equal).  The T * topk (token, expert) pairs are then
+ * ordered by expert, and by token within an expert: offsets[e] is the number
+ * of pairs with a smaller expert id (offsets[E] = T * topk), the pair at
+ * position p has token row_index[p], and slot_of[t, j] is the position of the
+ * pair (t, experts[t, j]).  Returns -1 on a bad shape or a non-finite logit. */
+int oracle_route(const float* logits, int64_t T, int64_t E, int64_t topk, int32_t* experts,
+                 int32_t* offsets, int32_t* row_index, int32_t* slot_of) {
+    if (T < 0 || E < 1 || topk < 1 || topk > E) return -1;
+    int bad = 0;
+    #pragma omp parallel for schedule(static) reduction(| : bad)
+    for (int64_t t = 0; t < T; ++t) {
+        const float* lt = logits + t * E;
+        for (int64_t e = 0; e < E; ++e)
+            if (!isfinite(lt[e])) bad = 1;
+        for (int64_t j = 0; j < topk; ++j) {
+            int64_t best = -1;
+            for (int64_t e = 0; e < E; ++e) {
+                int taken = 0;
+                for (int64_t i = 0; i < j; ++i)
+                    if (experts[t * topk + i] == e) taken = 1;
+                if (taken) continue;
+                /* strictly greater wins, so among equal logits the lowest id stays */
+                if (best < 0 || lt[e] > lt[best]) best = e;
+            }
+            experts[t * topk + j] = (int32_t)best;
+        }
+    }
+    if (bad) return -1;
+    int64_t p = 0;
+    for (int64_t e = 0; e < E; ++e) {
+        offsets[e] = (int32_t)p;
+        for (int64_t t = 0; t < T; ++t)
+            for (int64_t j = 0; j < topk; ++j)
+                if (experts[t * topk + j] == e) {
+                    row_index[p] = (int32_t)t;
+                    slot_of[t * topk + j] = (int32_t)p;
+                    ++p;
+                }
+    }
+    offsets[E] = (int32_t)p;
+    return 0;
+}
+
 /* ------------------------------------------------------------------ GEMM -- */
 
 /* s_b * e2m1(code) * 2^10 as an exact integer, tabulated once per call for

@@ -1,8 +1,8 @@
 """Seeded synthetic inputs for the per-token NVFP4 path.
 
 Shared by the tests, the benchmark and the oracle's self-checks.  This module
-draws random numbers and lays out routed rows; it holds none of the
-quantizer's or the GEMM's arithmetic.  The random streams are SplitMix64
+draws random numbers (activations, weights, router logits); it holds none of the
+quantizer's, the router's or the GEMM's arithmetic.  The random streams are SplitMix64
 (counter-based, see ``synthgen.c``), so a tensor's bytes depend only on
 (seed, stream, index), never on thread count or machine.
 
@@ -12,11 +12,12 @@ models are used):
 
   1 tiny dense     X 128x512 N(0,1) with 1% of entries x50, W 256x512 N(0,0.02)
   2 dense linear   X 4096x2560 Student-t(3)/sqrt(3), W 9728x2560 N(0,0.02)
-  3 MoE up         X 4096x2048 t3, 128 experts, top-8 routing from softmax of
-                   N(0,1) logits + Zipf(1.1) bias, W_up 128x1536x2048 N(0,0.02)
+  3 MoE up         X 4096x2048 t3, fp32 router logits N(0,1) + Zipf(1.1) expert
+                   bias for 128 experts (top-8 routing), W_up 128x1536x2048 N(0,0.02)
   4 MoE down       H 32768x768 t3 in the contiguous layout of config 3's
-                   routing, exact row amax supplied for reuse, W_dn 128x2048x768
-  5 rollout decode 64 tokens: X 64x2048 and H 512x768 t3, routing of its own,
+                   routing (its logits), exact row amax supplied for reuse,
+                   W_dn 128x2048x768
+  5 rollout decode 64 tokens: X 64x2048 and H 512x768 t3, router logits of its own,
                    the config 3/4 expert shapes, and dense 64x2560 -> 9728
 """
 import ctypes
@@ -131,32 +132,16 @@ def permutation(seed, stream, n):
     return np.array(perm, np.int64)
 
 
-def routing(seed, tokens, experts=128, topk=8, zipf_s=1.1):
-    """Top-k routing from softmax(N(0,1) logits + Zipf(s) expert bias).
-
-    Expert e has popularity rank r_e (a seeded permutation of 1..E) and bias
-    ln(r_e^-s / sum_r r^-s).  softmax is monotone per token, so the top-k of
-    the biased logits is the routing (ties go to the lower expert id).  The
-    routed (token, expert) pairs are sorted stably by (expert, token) into the
-    contiguous per-expert layout.
-
-    Returns dict(row_index int32 [tokens*topk], offsets int32 [experts+1],
-    expert_of_row int32 [tokens*topk], counts int64 [experts]).
-    """
+def router_logits(seed, tokens, experts=128, zipf_s=1.1):
+    """fp32 router logits [tokens, experts]: N(0,1) plus a Zipf(s) expert
+    bias.  Expert e has popularity rank r_e (a seeded permutation of 1..E) and
+    bias ln(r_e^-s / sum_r r^-s), so a few experts draw most tokens, as in a
+    trained MoE router.  Formed in fp64 and rounded to fp32 (nearest even)."""
     ranks = permutation(seed, S_PERM, experts) + 1
     w = np.arange(1, experts + 1, dtype=np.float64) ** (-zipf_s)
     bias = np.log(ranks.astype(np.float64) ** (-zipf_s) / w.sum())
-    logits = normal(seed, S_LOGITS, tokens * experts).reshape(tokens, experts) + bias[None, :]
-    order = np.argsort(-logits, axis=1, kind="stable")[:, :topk]
-    tok = np.repeat(np.arange(tokens), topk)
-    exp = order.reshape(-1)
-    srt = np.lexsort((tok, exp))
-    tok, exp = tok[srt], exp[srt]
-    counts = np.bincount(exp, minlength=experts)
-    offsets = np.zeros((experts + 1,), np.int64)
-    offsets[1:] = np.cumsum(counts)
-    return dict(row_index=tok.astype(np.int32), offsets=offsets.astype(np.int32),
-                expert_of_row=exp.astype(np.int32), counts=counts)
+    z = normal(seed, S_LOGITS, tokens * experts).reshape(tokens, experts) + bias[None, :]
+    return z.astype(np.float32)
 
 
 def row_amax_bf16(x_bf16):
@@ -187,23 +172,23 @@ def workload(c, part=None):
     elif c == 3:
         if want("x"):
             d["x"] = student_t3_bf16(seed, S_X, (4096, 2048))
-        if want("routing"):
-            d["routing"] = routing(seed, 4096)
+        if want("logits"):
+            d["logits"] = router_logits(seed, 4096)
         if want("w"):
             d["w"] = normal_bf16(seed, S_W, (128, 1536, 2048), 0.0, 0.02)
     elif c == 4:
         if want("h"):
             d["h"] = student_t3_bf16(seed, S_H, (32768, 768))
             d["h_amax"] = row_amax_bf16(d["h"])
-        if want("routing"):
-            d["routing"] = routing(config_seed(3), 4096)
+        if want("logits"):
+            d["logits"] = router_logits(config_seed(3), 4096)
         if want("w"):
             d["w"] = normal_bf16(seed, S_WDN, (128, 2048, 768), 0.0, 0.02)
     elif c == 5:
         if want("x"):
             d["x"] = student_t3_bf16(seed, S_X, (64, 2048))
-        if want("routing"):
-            d["routing"] = routing(seed, 64)
+        if want("logits"):
+            d["logits"] = router_logits(seed, 64)
         if want("h"):
             d["h"] = student_t3_bf16(seed, S_H, (512, 768))
             d["h_amax"] = row_amax_bf16(d["h"])

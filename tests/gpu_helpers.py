@@ -63,6 +63,12 @@ def workload(c, part):
 
 
 @functools.lru_cache(maxsize=None)
+def routing(c):
+    """The oracle's top-8 contiguous layout of workload c's router logits."""
+    return oracle.route(workload(c, "logits")["logits"], topk=8)
+
+
+@functools.lru_cache(maxsize=None)
 def oracle_weight(c, name):
     w = workload(c, name)[name]
     return oracle.quantize_weight(w)

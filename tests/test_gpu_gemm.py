@@ -14,7 +14,7 @@ import torch
 import nvfp4_token_quantization_amd as nv
 import oracle
 import synthgen as sg
-from gpu_helpers import check_gemm, dev, oracle_rows, oracle_weight, to_dev, to_np, workload
+from gpu_helpers import check_gemm, dev, oracle_rows, oracle_weight, routing, to_dev, to_np, workload
 
 pytestmark = pytest.mark.gpu
 
@@ -182,17 +182,17 @@ def _grouped_sample(offsets, n, count, seed):
 @pytest.mark.parametrize("cfg", [3, 4, 5])
 def test_grouped_workloads(cfg):
     if cfg == 3:
-        r = workload(3, "routing")["routing"]
+        r = routing(3)
         a = oracle_rows(3, "x")
         b = oracle_weight(3, "w")[:3]
         ri, offsets = r["row_index"], r["offsets"]
     elif cfg == 4:
-        r = workload(4, "routing")["routing"]
+        r = routing(4)
         a = oracle_rows(4, "h", True)
         b = oracle_weight(4, "w")[:3]
         ri, offsets = None, r["offsets"]
     else:
-        r = workload(5, "routing")["routing"]
+        r = routing(5)
         a = oracle_rows(5, "x")
         b = oracle_weight(5, "w")[:3]
         ri, offsets = r["row_index"], r["offsets"]
@@ -212,7 +212,7 @@ def test_grouped_workloads(cfg):
 
 
 def test_grouped_config5_down():
-    r = workload(5, "routing")["routing"]
+    r = routing(5)
     a = oracle_rows(5, "h", True)
     b = oracle.quantize_weight(workload(5, "w_dn")["w_dn"])[:3]
     offsets = r["offsets"]

@@ -15,7 +15,7 @@ import torch
 import nvfp4_token_quantization_amd as nv
 import oracle
 import synthgen as sg
-from gpu_helpers import assert_same_quant, dev, oracle_rows, oracle_weight, to_dev, to_np, workload
+from gpu_helpers import assert_same_quant, dev, oracle_weight, routing, to_dev, to_np, workload
 
 pytestmark = pytest.mark.gpu
 
@@ -142,10 +142,10 @@ def test_swiglu_chained_rollout_decode():
     """Chained variant on the rollout-decode workload: the oracle's exact
     grouped up-projection of the 64 tokens (512 routed rows, fused gate|up
     weight 128 x 1536 x 2048) rounded to fp32 feeds the fused kernel."""
-    d = workload(5, "x,routing")
+    d = workload(5, "x")
     xq = oracle.quantize_rows(d["x"])
     wq, wsb, ws, _ = oracle_weight(5, "w")
-    rt = d["routing"]
+    rt = routing(5)
     y, _ = oracle.grouped_gemm(xq, rt["offsets"], (wq, wsb, ws), row_index=rt["row_index"])
     gu = y.astype(np.float32)
     check_against_oracle(gu, run_all(gu), "chained rollout decode")
