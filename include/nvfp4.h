@@ -143,6 +143,38 @@ int nvfp4_swiglu_quantize_rows(const float* gate_up, int64_t rows, int64_t f, ui
                                void* stream);
 
 /*
+ * Top-k MoE routing into the contiguous per-expert layout, on the device.
+ *
+ * Defined by: the miniTE page, section Transformer Engine路径优化 (contiguous
+ * layouts and device-side metadata feed the grouped GEMMs; tokens are
+ * quantized once and gathered); each token goes to the experts with its
+ * top-k router logits (softmax is monotone, so the logits decide).
+ *
+ *   logits      [tokens, num_experts] f32, finite (non-finite logits give an
+ *               unspecified but in-range routing).
+ *   experts     [tokens, topk] i32 out: the chosen experts of each token,
+ *               largest logit first, the lower expert id first among equal
+ *               logits (+0 equals -0).
+ *   offsets     [num_experts + 1] i32 out: offsets[e] = routed rows of experts
+ *               below e; offsets[num_experts] = tokens * topk.
+ *   row_index   [tokens * topk] i32 out: token of each routed row; rows are
+ *               ordered by expert, then by token (the layout
+ *               nvfp4_grouped_gemm reads with row_index).
+ *   slot_of     [tokens, topk] i32 out: routed row of each (token, choice).
+ * 1 <= topk <= num_experts, num_experts <= 1024, topk <= 64,
+ * tokens * topk < 2^31.  The result is deterministic (no atomics).  The
+ * layout passes run one workgroup per expert, each reading all tokens * topk
+ * choices (from L2 at MoE batch sizes).
+ * Errors: INVALID_VALUE (negative tokens, topk < 1 or > num_experts, null
+ * pointers with work; offsets is always written), UNSUPPORTED_SHAPE
+ * (num_experts > 1024, topk > 64, too many rows), MISALIGNED (4 bytes), ARCH,
+ * LAUNCH.
+ */
+int nvfp4_moe_route(const float* logits, int64_t tokens, int64_t num_experts, int64_t topk,
+                    int32_t* experts, int32_t* offsets, int32_t* row_index, int32_t* slot_of,
+                    void* stream);
+
+/*
  * Dense block-scaled W4A4 GEMM: Y = deq(A) . deq(B)^T with the per-token
  * scale and the weight scale applied in the epilogue, Y = S_A[m] * S_B *
  * sum_k (s_bA q_A)(s_bB q_B).

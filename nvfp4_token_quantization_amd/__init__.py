@@ -54,10 +54,11 @@ def lib():
         L.nvfp4_gemm.argtypes = [P, P, P, I64, P, P, P, I64, I64, P, P]
         L.nvfp4_grouped_gemm.argtypes = [P, P, P, I64, P, I64, P, I64, P, P, P, I64, I64, P, P]
         L.nvfp4_swiglu_quantize_rows.argtypes = [P, I64, I64, P, P, P, P, P, P]
+        L.nvfp4_moe_route.argtypes = [P, I64, I64, I64, P, P, P, P, P]
         L.nvfp4_debug_encode_e2m1.argtypes = [P, I64, P, P]
         L.nvfp4_debug_encode_e4m3.argtypes = [P, I64, P, P]
         for f in ("nvfp4_quantize_rows", "nvfp4_quantize_weight", "nvfp4_gemm",
-                  "nvfp4_swiglu_quantize_rows",
+                  "nvfp4_swiglu_quantize_rows", "nvfp4_moe_route",
                   "nvfp4_grouped_gemm", "nvfp4_debug_encode_e2m1", "nvfp4_debug_encode_e4m3"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
@@ -161,6 +162,29 @@ def nvfp4_swiglu_quantize_rows(gate_up, want_h=False, want_amax=False, quantize=
                                           _ptr(res.get("amax")), _ptr(res.get("q")),
                                           _ptr(res.get("sb")), _ptr(res.get("s")), _stream(dev))
     _check("nvfp4_swiglu_quantize_rows", st)
+    return res
+
+
+def nvfp4_moe_route(logits, topk, out=None):
+    """Top-k routing of fp32 logits [tokens, experts] into the contiguous
+    per-expert layout on the device.  Returns a dict of int32 tensors:
+    experts [tokens, topk], offsets [experts+1], row_index [tokens*topk],
+    slot_of [tokens, topk]."""
+    _dev(logits, "logits", (torch.float32,), 2)
+    T, E = logits.shape
+    dev = logits.device
+    out = dict(out or {})
+    i32 = torch.int32
+    res = {}
+    for key, shape in (("experts", (T, topk)), ("offsets", (E + 1,)), ("row_index", (T * topk,)),
+                       ("slot_of", (T, topk))):
+        res[key] = out.get(key, None)
+        if res[key] is None:
+            res[key] = torch.empty(shape, dtype=i32, device=dev)
+    st = lib().nvfp4_moe_route(_ptr(logits), T, E, int(topk), _ptr(res["experts"]),
+                               _ptr(res["offsets"]), _ptr(res["row_index"]), _ptr(res["slot_of"]),
+                               _stream(dev))
+    _check("nvfp4_moe_route", st)
     return res
 
 

@@ -122,6 +122,20 @@ def test_swiglu_quantize_argument_errors(L):
     assert f(None, 0, 16, None, None, None, None, None, None) == OK     # no rows: nothing to do
 
 
+def test_moe_route_argument_errors(L):
+    f = L.nvfp4_moe_route
+    a = P(FAKE)
+    assert f(a, -1, 128, 8, a, a, a, a, None) == INVALID
+    assert f(a, 4, 128, 0, a, a, a, a, None) == INVALID            # topk < 1
+    assert f(a, 4, 8, 9, a, a, a, a, None) == INVALID              # topk > experts
+    assert f(a, 4, 2048, 8, a, a, a, a, None) == SHAPE             # > 1024 experts
+    assert f(a, 4, 128, 65, a, a, a, a, None) == SHAPE             # topk > 64
+    assert f(a, 1 << 28, 128, 8, a, a, a, a, None) == SHAPE        # >= 2^31 routed rows
+    assert f(a, 4, 128, 8, a, None, a, a, None) == INVALID         # offsets always needed
+    assert f(None, 4, 128, 8, a, a, a, a, None) == INVALID
+    assert f(a, 4, 128, 8, a, a, P(FAKE + 2), a, None) == MISALIGNED
+
+
 def test_debug_hooks_argument_errors(L):
     assert L.nvfp4_debug_encode_e2m1(None, 4, P(FAKE), None) == INVALID
     assert L.nvfp4_debug_encode_e4m3(P(FAKE), -1, P(FAKE), None) == INVALID
