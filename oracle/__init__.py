@@ -69,6 +69,8 @@ def lib():
         L.oracle_quantize_weight.restype = ctypes.c_int
         L.oracle_dequantize.argtypes = [P, P, P, P, I64, I64, P]
         L.oracle_f32_to_bf16_array.argtypes = [P, I64, P]
+        L.oracle_f64_to_bf16_array.argtypes = [P, I64, P]
+        L.oracle_dequantize_bf16.argtypes = [P, P, P, I64, I64, I64, P]
         L.oracle_swiglu_rows.argtypes = [P, I64, I64, P]
         L.oracle_swiglu_rows.restype = ctypes.c_int
         L.oracle_route.argtypes = [P, I64, I64, I64, P, P, P, P]
@@ -184,6 +186,27 @@ def f32_to_bf16(v):
     v = _c(v, np.float32)
     out = np.empty(v.shape, np.uint16)
     lib().oracle_f32_to_bf16_array(_p(v), v.size, _p(out))
+    return out
+
+
+def f64_to_bf16(v):
+    """bf16 bit patterns nearest to float64 values (one rounding, ties to even)."""
+    v = _c(v, np.float64)
+    out = np.empty(v.shape, np.uint16)
+    lib().oracle_f64_to_bf16_array(_p(v), v.size, _p(out))
+    return out
+
+
+def dequantize_bf16(q, sb, s, rows_per_scale=1):
+    """bf16(S * s_b * e2m1(q)) rounded once; q [rows, k/2], sb [rows, k/16],
+    s [rows / rows_per_scale].  Returns uint16 bf16 bits [rows, k]."""
+    q = _c(q, np.uint8)
+    sb = _c(sb, np.uint8)
+    s = _c(np.atleast_1d(s), np.float32)
+    rows = q.shape[0]
+    k = q.shape[1] * 2
+    out = np.empty((rows, k), np.uint16)
+    lib().oracle_dequantize_bf16(_p(q), _p(sb), _p(s), rows, k, int(rows_per_scale), _p(out))
     return out
 
 

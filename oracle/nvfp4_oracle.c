@@ -254,6 +254,38 @@ static uint16_t f32_to_bf16_nearest(float v) {
     return (lo & 1) ? hi : lo;
 }
 
+/* bf16 bit pattern nearest to a finite double x (ties to the even pattern;
+ * values at or past the halfway point above the largest bf16 give infinity).
+ * The bf16 grid near x has spacing 2^(e - 7) where 2^e <= |x| < 2^(e+1),
+ * e >= -126 (below that the subnormal spacing 2^-133); the two grid points
+ * around |x| are found by exact power-of-two scaling and floor. */
+static uint16_t f64_to_bf16_nearest(double x) {
+    uint16_t sign = signbit(x) ? 0x8000 : 0;
+    double a = fabs(x);
+    if (a == 0.0) return sign;
+    int e;
+    frexp(a, &e);         /* a = f * 2^e, 0.5 <= f < 1 */
+    e -= 1;               /* 2^e <= a < 2^(e+1) */
+    if (e < -126) e = -126;
+    double ulp = ldexp(1.0, e - 7);
+    double m = floor(a / ulp);          /* grid index of the lower neighbour */
+    double lo = m * ulp, hi = (m + 1.0) * ulp;
+    double dl = a - lo, dh = hi - a;    /* exact: a has far fewer bits than a double */
+    double r = (dl < dh) ? m : (dh < dl) ? m + 1.0 : (fmod(m, 2.0) == 0.0 ? m : m + 1.0);
+    double v = r * ulp;
+    if (v >= ldexp(1.0, 128)) return (uint16_t)(sign | 0x7F80);
+    /* bit pattern of the finite bf16 value v */
+    float fv = (float)v;                /* exact: v is on the bf16 grid */
+    uint32_t u;
+    memcpy(&u, &fv, 4);
+    return (uint16_t)(sign | (u >> 16));
+}
+
+void oracle_f64_to_bf16_array(const double* v, int64_t n, uint16_t* out) {
+    #pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; ++i) out[i] = f64_to_bf16_nearest(v[i]);
+}
+
 void oracle_f32_to_bf16_array(const float* v, int64_t n, uint16_t* out) {
     #pragma omp parallel for schedule(static)
     for (int64_t i = 0; i < n; ++i) out[i] = f32_to_bf16_nearest(v[i]);
@@ -341,6 +373,27 @@ int oracle_route(const float* logits, int64_t T, int64_t E, int64_t topk, int32_
     }
     offsets[E] = (int32_t)p;
     return 0;
+}
+
+/* Dequantize to bf16, for backward GEMMs that consume the dequantized
+ * forward operands (Miles page, section 反量化反向模式: the backward runs in
+ * BF16 on the BF16 dequantization of the exact low-precision operands):
+ * x_bf16 = bf16(S * s_b * e2m1(q)), the product formed exactly (at most 30
+ * significant bits) and rounded once to nearest even.  Row r uses the outer
+ * scale s[r / rows_per_scale] (1 for per-token scales, the group's row count
+ * for per-tensor / per-expert weights). */
+void oracle_dequantize_bf16(const uint8_t* q, const uint8_t* sb, const float* s,
+                            int64_t rows, int64_t k, int64_t rows_per_scale, uint16_t* out) {
+    #pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r) {
+        double S = (double)s[r / rows_per_scale];
+        for (int64_t j = 0; j < k; ++j) {
+            uint8_t byte = q[r * (k / 2) + j / 2];
+            int code = (j & 1) ? (byte >> 4) : (byte & 15);
+            double sbv = oracle_e4m3_value(sb[r * (k / 16) + j / 16]);
+            out[r * k + j] = f64_to_bf16_nearest(S * sbv * oracle_e2m1_value(code));
+        }
+    }
 }
 
 /* ------------------------------------------------------------------ GEMM -- */
