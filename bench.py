@@ -380,6 +380,18 @@ def main():
     nxt["moe_route"] = {"ms": round(ms, 4), "GB/s": round(byt / ms / 1e6, 1),
                         "frac_hbm": round(byt / ms / 1e6 / HBM_PEAK_GBS, 4), "bytes": int(byt),
                         "tokens_per_s": round(TT / ms * 1e3, 1)}
+    # bf16 dequantization of forward operands for a dequantized backward:
+    # the MoE down input H (per-token scales) and the fused W_up (per expert)
+    for name, (qq, ss, rows, kk, rps) in (
+            ("dequantize_rows_h", (out["h4"], out["h4"][2], MH, K4, 1)),
+            ("dequantize_weight_up", (out["w3"], out["w3"][2], E * N3, K3, N3))):
+        dq = empty((rows, kk), torch.bfloat16)
+        ms = time_extra(lambda: L.nvfp4_dequantize_rows(
+            p(qq[0]), p(qq[1]), p(ss), rows, kk, rps, p(dq), sp), K)
+        byt = rows * kk // 2 + rows * kk // 16 + (rows // rps) * 4 + rows * kk * 2
+        nxt[name] = {"ms": round(ms, 4), "GB/s": round(byt / ms / 1e6, 1),
+                     "frac_hbm": round(byt / ms / 1e6 / HBM_PEAK_GBS, 4), "bytes": int(byt)}
+        del dq
     log("next rows: %s" % nxt)
 
     # dominant kernel = longest per step

@@ -175,6 +175,28 @@ int nvfp4_moe_route(const float* logits, int64_t tokens, int64_t num_experts, in
                     void* stream);
 
 /*
+ * NVFP4 -> bf16 dequantization, for backward GEMMs that consume the
+ * dequantized forward operands.
+ *
+ * Defined by: the Miles page, section 反量化反向模式 (the dequantized backward
+ * runs its GEMMs in BF16 on the BF16 dequantization of the exact
+ * low-precision forward operands) and the decode x_hat = S * s_b * e2m1(q)
+ * of the TRIAGE page, section 前置知识.
+ *
+ *   q [rows, k/2] u8, sb [rows, k/16] u8 (E4M3 codes 0..0x7E; the sign bit
+ *   is ignored, NaN codes give unspecified values), s [ceil(rows /
+ *   rows_per_scale)] f32: row r uses s[r / rows_per_scale] (1 for per-token
+ *   scales, rows_per_group for per-tensor / per-expert weights).
+ *   x_bf16 [rows, k] bf16 out: bf16(S * s_b * e2m1(q)), the product exact
+ *   and rounded once to nearest even; -0 codes give -0.
+ * Errors: INVALID_VALUE (negative sizes, rows_per_scale < 1, null pointers
+ * with work), UNSUPPORTED_SHAPE (k % 16 != 0), MISALIGNED (q and x_bf16 16
+ * bytes, s 4), ARCH, LAUNCH.
+ */
+int nvfp4_dequantize_rows(const uint8_t* q, const uint8_t* sb, const float* s, int64_t rows,
+                          int64_t k, int64_t rows_per_scale, uint16_t* x_bf16, void* stream);
+
+/*
  * Dense block-scaled W4A4 GEMM: Y = deq(A) . deq(B)^T with the per-token
  * scale and the weight scale applied in the epilogue, Y = S_A[m] * S_B *
  * sum_k (s_bA q_A)(s_bB q_B).

@@ -22,6 +22,7 @@ Layouts (all row-major): x bf16 [rows, k]; q uint8 [rows, k/2] with element
 import ctypes
 import os
 
+import numpy as np
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -55,10 +56,11 @@ def lib():
         L.nvfp4_grouped_gemm.argtypes = [P, P, P, I64, P, I64, P, I64, P, P, P, I64, I64, P, P]
         L.nvfp4_swiglu_quantize_rows.argtypes = [P, I64, I64, P, P, P, P, P, P]
         L.nvfp4_moe_route.argtypes = [P, I64, I64, I64, P, P, P, P, P]
+        L.nvfp4_dequantize_rows.argtypes = [P, P, P, I64, I64, I64, P, P]
         L.nvfp4_debug_encode_e2m1.argtypes = [P, I64, P, P]
         L.nvfp4_debug_encode_e4m3.argtypes = [P, I64, P, P]
         for f in ("nvfp4_quantize_rows", "nvfp4_quantize_weight", "nvfp4_gemm",
-                  "nvfp4_swiglu_quantize_rows", "nvfp4_moe_route",
+                  "nvfp4_swiglu_quantize_rows", "nvfp4_moe_route", "nvfp4_dequantize_rows",
                   "nvfp4_grouped_gemm", "nvfp4_debug_encode_e2m1", "nvfp4_debug_encode_e4m3"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
@@ -163,6 +165,27 @@ def nvfp4_swiglu_quantize_rows(gate_up, want_h=False, want_amax=False, quantize=
                                           _ptr(res.get("sb")), _ptr(res.get("s")), _stream(dev))
     _check("nvfp4_swiglu_quantize_rows", st)
     return res
+
+
+def nvfp4_dequantize_rows(q, sb, s, rows_per_scale=1, out=None):
+    """bf16 dequantization of NVFP4 rows: q [rows, k/2] (or [groups, rows,
+    k/2]), sb matching, s float32 with one entry per rows_per_scale rows.
+    Returns bf16 [rows, k] (same leading shape as q)."""
+    _dev(q, "q", (torch.uint8,))
+    _dev(sb, "sb", (torch.uint8,))
+    _dev(s, "s", (torch.float32,))
+    k = q.shape[-1] * 2
+    rows = q.numel() // max(q.shape[-1], 1) if q.shape[-1] else int(np.prod(q.shape[:-1]))
+    if sb.numel() != rows * (k // 16):
+        raise ValueError("sb must hold k/16 scale codes per row")
+    if s.numel() * rows_per_scale < rows:
+        raise ValueError("s must hold one outer scale per rows_per_scale rows")
+    if out is None:
+        out = torch.empty(tuple(q.shape[:-1]) + (k,), dtype=torch.bfloat16, device=q.device)
+    st = lib().nvfp4_dequantize_rows(_ptr(q), _ptr(sb), _ptr(s), rows, k, int(rows_per_scale),
+                                     _ptr(out), _stream(q.device))
+    _check("nvfp4_dequantize_rows", st)
+    return out
 
 
 def nvfp4_moe_route(logits, topk, out=None):

@@ -7,7 +7,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libnvfp4.so")
-SOURCES = ["abi_common.hip", "quantize.hip", "swiglu_quantize.hip", "route.hip", "gemm.hip"]
+SOURCES = ["abi_common.hip", "quantize.hip", "swiglu_quantize.hip", "route.hip", "dequantize.hip",
+           "gemm.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

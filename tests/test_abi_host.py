@@ -136,6 +136,19 @@ def test_moe_route_argument_errors(L):
     assert f(a, 4, 128, 8, a, a, P(FAKE + 2), a, None) == MISALIGNED
 
 
+def test_dequantize_argument_errors(L):
+    f = L.nvfp4_dequantize_rows
+    a = P(FAKE)
+    assert f(a, a, a, -1, 16, 1, a, None) == INVALID
+    assert f(a, a, a, 4, 16, 0, a, None) == INVALID              # rows_per_scale < 1
+    assert f(a, a, a, 4, 24, 1, a, None) == SHAPE
+    assert f(None, a, a, 4, 16, 1, a, None) == INVALID
+    assert f(a, a, a, 4, 16, 1, None, None) == INVALID
+    assert f(P(FAKE + 8), a, a, 4, 16, 1, a, None) == MISALIGNED
+    assert f(a, a, a, 4, 16, 1, P(FAKE + 2), None) == MISALIGNED
+    assert f(None, None, None, 0, 16, 1, None, None) == OK
+
+
 def test_debug_hooks_argument_errors(L):
     assert L.nvfp4_debug_encode_e2m1(None, 4, P(FAKE), None) == INVALID
     assert L.nvfp4_debug_encode_e4m3(P(FAKE), -1, P(FAKE), None) == INVALID
