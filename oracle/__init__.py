@@ -74,6 +74,9 @@ def lib():
         L.oracle_swiglu_rows.argtypes = [P, I64, I64, P]
         L.oracle_swiglu_rows.restype = ctypes.c_int
         L.oracle_route.argtypes = [P, I64, I64, I64, P, P, P, P]
+        L.oracle_mxfp8_quantize_rows.argtypes = [P, I64, I64, P, P]
+        L.oracle_mxfp8_quantize_rows.restype = ctypes.c_int
+        L.oracle_mxfp8_gemm.argtypes = [P, P, I64, P, P, I64, I64, P, P]
         L.oracle_route.restype = ctypes.c_int
         L.oracle_gemm_entries.argtypes = [P, P, P, P, P, P, I64, P, P, P, I64, P, P]
         L.oracle_gemm.argtypes = [P, P, P, I64, P, P, P, I64, I64, P, P]
@@ -253,6 +256,41 @@ def route(logits, topk=8):
         raise ValueError("oracle_route: bad shape or non-finite logit")
     return dict(experts=experts, offsets=offsets, row_index=row_index, slot_of=slot_of,
                 counts=np.diff(offsets).astype(np.int64))
+
+
+# ------------------------------------------------------------------- MXFP8 --
+def mxfp8_quantize_rows(x_bf16):
+    """MXFP8 of bf16 rows [rows, k] (k % 32 == 0): E4M3 codes [rows, k] and
+    E8M0 scale codes [rows, k/32] (2^(code - 127), rounded up)."""
+    x = _c(x_bf16, np.uint16)
+    rows, k = x.shape
+    q = np.empty((rows, k), np.uint8)
+    sc = np.empty((rows, k // 32), np.uint8)
+    if lib().oracle_mxfp8_quantize_rows(_p(x), rows, k, _p(q), _p(sc)) != 0:
+        raise ValueError("oracle_mxfp8_quantize_rows: bad shape or non-finite input")
+    return q, sc
+
+
+def mxfp8_dequantize(q, sc):
+    """fp64 values of MXFP8 rows (exact)."""
+    q = _c(q, np.uint8)
+    sc = _c(sc, np.uint8)
+    mag = e4m3_table()[q & 0x7F]
+    v = np.where(q & 0x80, -mag, mag)
+    return v * np.repeat(np.ldexp(1.0, sc.astype(np.int64) - 127), 32, axis=1)
+
+
+def mxfp8_gemm(a, b):
+    """(y_ref, bound) for Y = deq(A) . deq(B)^T, a = (q [m, k], sc [m, k/32]),
+    b = (q [n, k], sc [n, k/32])."""
+    aq, asc = _c(a[0], np.uint8), _c(a[1], np.uint8)
+    bq, bsc = _c(b[0], np.uint8), _c(b[1], np.uint8)
+    m, k = aq.shape
+    n = bq.shape[0]
+    y = np.empty((m, n), np.float64)
+    bound = np.empty((m, n), np.float64)
+    lib().oracle_mxfp8_gemm(_p(aq), _p(asc), m, _p(bq), _p(bsc), n, k, _p(y), _p(bound))
+    return y, bound
 
 
 # -------------------------------------------------------------------- GEMM --

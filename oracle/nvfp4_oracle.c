@@ -396,6 +396,87 @@ void oracle_dequantize_bf16(const uint8_t* q, const uint8_t* sb, const float* s,
     }
 }
 
+/* ---------------------------------------------------------------- MXFP8 -- */
+
+/* MXFP8 (Miles page, section MXFP8格式背景): each run of 32 consecutive
+ * values along the contraction axis is stored as E4M3 codes under one E8M0
+ * scale, a power of two 2^e (code e + 127, codes 0..254).  The scale is
+ * rounded up: 2^e is the smallest power of two with a_b / 2^e <= 448 (the
+ * E4M3 maximum), so the block maximum is never clipped; an all-zero block
+ * (and any block needing e < -127) takes code 0.  Elements are
+ * RNE_SAT_E4M3(|x| / 2^e) with the sign bit of x (bit 7).
+ * x is bf16 [rows, k], k % 32 == 0.  q [rows, k] E4M3 codes, sc [rows, k/32].
+ * Returns -1 on a bad shape or a non-finite input, else 0. */
+static int mx_scale_exponent(double amax) {
+    if (amax == 0.0) return -127;
+    int e = -127;
+    while (ldexp(448.0, e) < amax) ++e;   /* smallest e with amax <= 448 * 2^e */
+    return e;
+}
+
+int oracle_mxfp8_quantize_rows(const uint16_t* x, int64_t rows, int64_t k, uint8_t* q,
+                               uint8_t* sc) {
+    if (rows < 0 || k < 0 || k % 32 != 0) return -1;
+    int bad = 0;
+    #pragma omp parallel for schedule(static) reduction(| : bad)
+    for (int64_t r = 0; r < rows; ++r) {
+        for (int64_t b = 0; b < k / 32; ++b) {
+            const uint16_t* xb = x + r * k + 32 * b;
+            double amax = 0.0;
+            for (int j = 0; j < 32; ++j) {
+                double v = fabs((double)bf16_to_f32(xb[j]));
+                if (!isfinite(v)) bad = 1;
+                if (v > amax) amax = v;
+            }
+            int e = mx_scale_exponent(amax);
+            sc[r * (k / 32) + b] = (uint8_t)(e + 127);
+            for (int j = 0; j < 32; ++j) {
+                float xv = bf16_to_f32(xb[j]);
+                /* |x| / 2^e is exact in double; the E4M3 search rounds it */
+                double v = ldexp(fabs((double)xv), -e);
+                int mag = rne_sat_search(v, 128, oracle_e4m3_value);
+                q[r * k + 32 * b + j] = (uint8_t)((signbit(xv) ? 0x80 : 0) | mag);
+            }
+        }
+    }
+    return bad ? -1 : 0;
+}
+
+/* MXFP8 GEMM reference: Y[m,n] = sum over blocks of 2^(e_A + e_B) * sum of
+ * the 32 products of E4M3 values.  Within a block the products are integers
+ * times 2^-18 and their sum is formed exactly in int64; the blocks are summed
+ * in fp64 (error at most (k/32) * 2^-53 * sum |a b|).  bound = sum |a_k b_k|
+ * in fp64.  A [m, k] codes + [m, k/32] scales, B [n, k] + [n, k/32]. */
+static int64_t e4m3_int(uint8_t c) {   /* E4M3 value * 2^9, exact integer */
+    double v = oracle_e4m3_value(c & 0x7F) * 512.0;
+    int64_t iv = (int64_t)v;
+    return (c & 0x80) ? -iv : iv;
+}
+
+void oracle_mxfp8_gemm(const uint8_t* a_q, const uint8_t* a_sc, int64_t m, const uint8_t* b_q,
+                       const uint8_t* b_sc, int64_t n, int64_t k, double* y, double* bound) {
+    int64_t nb = k / 32;
+    #pragma omp parallel for schedule(dynamic, 4)
+    for (int64_t i = 0; i < m; ++i) {
+        for (int64_t j = 0; j < n; ++j) {
+            double acc = 0.0, bnd = 0.0;
+            for (int64_t b = 0; b < nb; ++b) {
+                int64_t s = 0, sa = 0;
+                for (int t = 0; t < 32; ++t) {
+                    int64_t p = e4m3_int(a_q[i * k + 32 * b + t]) * e4m3_int(b_q[j * k + 32 * b + t]);
+                    s += p;
+                    sa += p < 0 ? -p : p;
+                }
+                int ex = (int)a_sc[i * nb + b] + (int)b_sc[j * nb + b] - 254 - 18;
+                acc += ldexp((double)s, ex);
+                bnd += ldexp((double)sa, ex);
+            }
+            y[i * n + j] = acc;
+            bound[i * n + j] = bnd;
+        }
+    }
+}
+
 /* ------------------------------------------------------------------ GEMM -- */
 
 /* s_b * e2m1(code) * 2^10 as an exact integer, tabulated once per call for
