@@ -42,6 +42,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, GB/s
 MFMA_F16_PEAK_TFS = 2500.0   # MI355X dense fp16/bf16 MFMA, TFLOP/s
+MFMA_FP8_PEAK_TFS = 5000.0   # MI355X dense fp8 MFMA, TFLOP/s
 
 
 def log(*a):
@@ -392,6 +393,32 @@ def main():
         nxt[name] = {"ms": round(ms, 4), "GB/s": round(byt / ms / 1e6, 1),
                      "frac_hbm": round(byt / ms / 1e6 / HBM_PEAK_GBS, 4), "bytes": int(byt)}
         del dq
+    # MXFP8 variant: quantize the dense activation, then the dense and the
+    # grouped up-projection GEMMs on the scaled fp8 MFMA
+    mx_x2 = (empty((M2, K2), u8), empty((M2, K2 // 32), u8))
+    mx_w2 = (empty((N2, K2), u8), empty((N2, K2 // 32), u8))
+    mx_x3 = (empty((T3, K3), u8), empty((T3, K3 // 32), u8))
+    mx_w3 = (empty((E * N3, K3), u8), empty((E * N3, K3 // 32), u8))
+    for src, dst, rows, kk in ((W2, mx_w2, N2, K2), (X3[0], mx_x3, T3, K3), (W3, mx_w3, E * N3, K3)):
+        st = L.nvfp4_mxfp8_quantize_rows(p(src), rows, kk, p(dst[0]), p(dst[1]), sp)
+        if st != 0:
+            raise RuntimeError("mxfp8 quantize failed: %s" % nv.status_string(st))
+    ms = time_extra(lambda: L.nvfp4_mxfp8_quantize_rows(p(X2[0]), M2, K2, p(mx_x2[0]), p(mx_x2[1]), sp), K)
+    byt = M2 * K2 * 2 + M2 * K2 + M2 * K2 // 32
+    nxt["mxfp8_quantize_rows_dense"] = {"ms": round(ms, 4), "GB/s": round(byt / ms / 1e6, 1),
+                                        "frac_hbm": round(byt / ms / 1e6 / HBM_PEAK_GBS, 4), "bytes": int(byt)}
+    ms = time_extra(lambda: L.nvfp4_mxfp8_gemm(p(mx_x2[0]), p(mx_x2[1]), M2, p(mx_w2[0]), p(mx_w2[1]),
+                                               N2, K2, p(out["y2"]), sp), K)
+    fl = 2.0 * M2 * N2 * K2
+    nxt["mxfp8_gemm_dense"] = {"ms": round(ms, 4), "TFLOP/s": round(fl / ms / 1e9, 1),
+                               "frac_mfma_fp8": round(fl / ms / 1e9 / MFMA_FP8_PEAK_TFS, 4), "flop": fl}
+    ms = time_extra(lambda: L.nvfp4_mxfp8_grouped_gemm(
+        p(mx_x3[0]), p(mx_x3[1]), T3, p(row_index), MR, p(offsets), E, p(mx_w3[0]), p(mx_w3[1]),
+        N3, K3, p(out["y3"]), sp), K)
+    fl = 2.0 * MR * N3 * K3
+    nxt["mxfp8_grouped_gemm_up"] = {"ms": round(ms, 4), "TFLOP/s": round(fl / ms / 1e9, 1),
+                                    "frac_mfma_fp8": round(fl / ms / 1e9 / MFMA_FP8_PEAK_TFS, 4), "flop": fl}
+    del mx_x2, mx_w2, mx_x3, mx_w3
     log("next rows: %s" % nxt)
 
     # dominant kernel = longest per step

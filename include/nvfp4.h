@@ -197,6 +197,64 @@ int nvfp4_dequantize_rows(const uint8_t* q, const uint8_t* sb, const float* s, i
                           int64_t k, int64_t rows_per_scale, uint16_t* x_bf16, void* stream);
 
 /*
+ * MXFP8 quantization: 32 consecutive values along k share one E8M0
+ * power-of-two scale; the values are E4M3.
+ *
+ * Defined by: the Miles page, section MXFP8格式背景 (1D blocks of 32 E4M3
+ * values with a local E8M0 scale, the decoded scale rounded up so the block
+ * maximum is not clipped).  Scale 2^e = the smallest power of two with
+ * a_b / 2^e <= 448 (a_b = block amax); code e + 127, clamped to [0, 254];
+ * zero blocks take code 0.  Element code = RNE_SAT_E4M3(|x| / 2^e) with the
+ * sign of x in bit 7.
+ *
+ *   x_bf16 [rows, k] bf16 bits, k % 32 == 0, finite.
+ *   q  [rows, k] u8 out (E4M3 codes);  sc [rows, k/32] u8 out (E8M0 codes).
+ * Errors: INVALID_VALUE, UNSUPPORTED_SHAPE (k % 32 != 0), MISALIGNED (x and
+ * q 16 bytes), ARCH, LAUNCH.
+ */
+int nvfp4_mxfp8_quantize_rows(const uint16_t* x_bf16, int64_t rows, int64_t k, uint8_t* q,
+                              uint8_t* sc, void* stream);
+
+/*
+ * MXFP8 GEMM on gfx950's scaled MFMA: Y = deq(A) . deq(B)^T with
+ * deq = 2^(sc - 127) * e4m3(q) per 32-block along k, fp32 accumulation and
+ * output.
+ *
+ * Defined by: the Miles page, section MXFP8格式背景 (the format), and section
+ * 配方1：端到端MXFP8 RL的设计 (forward, rollout and both gradient GEMMs run
+ * in MXFP8); blocks follow the contraction axis for both operands (section
+ * 案例研究：MXFP8 MLA投影张量).
+ *
+ *   a_q [m, k] u8 E4M3 codes, a_sc [m, k/32] u8 E8M0 codes (as written by
+ *   nvfp4_mxfp8_quantize_rows); b_q [n, k], b_sc [n, k/32]; y [m, n] f32 out.
+ *   k % 32 == 0 (k % 64 == 0 takes the fast path).  Scale code 0xFF (NaN)
+ *   gives NaN outputs.
+ * Accuracy: |Y - Y_ref| < 2^-9 * sum_k |a_k b_k|: the fp8 MFMA sums each
+ * 32-block's products in a fixed-point window about 15 bits below the
+ * block's largest product, truncating the rest (measured); block sums are
+ * accumulated in fp32.
+ * Errors: INVALID_VALUE, UNSUPPORTED_SHAPE (k % 32 != 0), MISALIGNED (a_q,
+ * b_q, y 16 bytes), ARCH, LAUNCH.
+ */
+int nvfp4_mxfp8_gemm(const uint8_t* a_q, const uint8_t* a_sc, int64_t m, const uint8_t* b_q,
+                     const uint8_t* b_sc, int64_t n, int64_t k, float* y, void* stream);
+
+/*
+ * Grouped (MoE) MXFP8 GEMM over the contiguous per-expert layout: output
+ * rows [offsets[g], offsets[g+1]) use expert g's weight; row_index as for
+ * nvfp4_grouped_gemm (quantize each token once, gather its routed copies).
+ *   a_q [a_rows, k], a_sc [a_rows, k/32]; row_index NULL or [m_total] i32;
+ *   offsets [groups+1] i32 device; b_q [groups, n, k], b_sc [groups, n, k/32];
+ *   y [m_total, n] f32 out (rows at or past offsets[groups] not written).
+ * groups <= 1024.  Errors as for nvfp4_grouped_gemm (k % 32 != 0 is
+ * UNSUPPORTED_SHAPE).
+ */
+int nvfp4_mxfp8_grouped_gemm(const uint8_t* a_q, const uint8_t* a_sc, int64_t a_rows,
+                             const int32_t* row_index, int64_t m_total, const int32_t* offsets,
+                             int64_t groups, const uint8_t* b_q, const uint8_t* b_sc, int64_t n,
+                             int64_t k, float* y, void* stream);
+
+/*
  * Dense block-scaled W4A4 GEMM: Y = deq(A) . deq(B)^T with the per-token
  * scale and the weight scale applied in the epilogue, Y = S_A[m] * S_B *
  * sum_k (s_bA q_A)(s_bB q_B).
@@ -256,6 +314,10 @@ int nvfp4_grouped_gemm(const uint8_t* a_q, const uint8_t* a_sb, const float* a_s
  * v [n] f32 device, code [n] u8 device.  Errors as above.
  */
 int nvfp4_debug_encode_e2m1(const float* v, int64_t n, uint8_t* code, void* stream);
+/* nvfp4_debug_encode_fp8: code[i] = E4M3 code (sign | RNE_SAT magnitude) of
+ * v[i] through the pack-convert the MXFP8 quantizer uses; only |v| <= 448
+ * and +-0 are specified (the quantizer never converts larger values). */
+int nvfp4_debug_encode_fp8(const float* v, int64_t n, uint8_t* code, void* stream);
 int nvfp4_debug_encode_e4m3(const float* v, int64_t n, uint8_t* code, void* stream);
 
 #ifdef __cplusplus

@@ -57,10 +57,16 @@ def lib():
         L.nvfp4_swiglu_quantize_rows.argtypes = [P, I64, I64, P, P, P, P, P, P]
         L.nvfp4_moe_route.argtypes = [P, I64, I64, I64, P, P, P, P, P]
         L.nvfp4_dequantize_rows.argtypes = [P, P, P, I64, I64, I64, P, P]
+        L.nvfp4_mxfp8_quantize_rows.argtypes = [P, I64, I64, P, P, P]
+        L.nvfp4_mxfp8_gemm.argtypes = [P, P, I64, P, P, I64, I64, P, P]
+        L.nvfp4_mxfp8_grouped_gemm.argtypes = [P, P, I64, P, I64, P, I64, P, P, I64, I64, P, P]
+        L.nvfp4_debug_encode_fp8.argtypes = [P, I64, P, P]
         L.nvfp4_debug_encode_e2m1.argtypes = [P, I64, P, P]
         L.nvfp4_debug_encode_e4m3.argtypes = [P, I64, P, P]
         for f in ("nvfp4_quantize_rows", "nvfp4_quantize_weight", "nvfp4_gemm",
                   "nvfp4_swiglu_quantize_rows", "nvfp4_moe_route", "nvfp4_dequantize_rows",
+                  "nvfp4_mxfp8_quantize_rows", "nvfp4_debug_encode_fp8", "nvfp4_mxfp8_gemm",
+                  "nvfp4_mxfp8_grouped_gemm",
                   "nvfp4_grouped_gemm", "nvfp4_debug_encode_e2m1", "nvfp4_debug_encode_e4m3"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
@@ -188,6 +194,55 @@ def nvfp4_dequantize_rows(q, sb, s, rows_per_scale=1, out=None):
     return out
 
 
+def nvfp4_mxfp8_quantize_rows(x, out=None):
+    """MXFP8 of bf16 rows x [rows, k] (k % 32 == 0): returns (q uint8 [rows,
+    k] E4M3 codes, sc uint8 [rows, k/32] E8M0 codes)."""
+    _dev(x, "x", _BF16, 2)
+    rows, k = x.shape
+    if out is None:
+        q = torch.empty((rows, k), dtype=torch.uint8, device=x.device)
+        sc = torch.empty((rows, k // 32), dtype=torch.uint8, device=x.device)
+    else:
+        q, sc = out
+    st = lib().nvfp4_mxfp8_quantize_rows(_ptr(x), rows, k, _ptr(q), _ptr(sc), _stream(x.device))
+    _check("nvfp4_mxfp8_quantize_rows", st)
+    return q, sc
+
+
+def nvfp4_mxfp8_gemm(a, b, out=None):
+    """Y = deq(A) . deq(B)^T for MXFP8 operands a = (q [m, k], sc [m, k/32]),
+    b = (q [n, k], sc [n, k/32]); fp32 [m, n]."""
+    aq, asc = a
+    bq, bsc = b
+    for t, nm in ((aq, "a_q"), (asc, "a_sc"), (bq, "b_q"), (bsc, "b_sc")):
+        _dev(t, nm, (torch.uint8,))
+    m, k = aq.shape[0], aq.shape[-1]
+    n = bq.shape[0]
+    y = out if out is not None else torch.empty((m, n), dtype=torch.float32, device=aq.device)
+    st = lib().nvfp4_mxfp8_gemm(_ptr(aq), _ptr(asc), m, _ptr(bq), _ptr(bsc), n, k, _ptr(y),
+                                _stream(aq.device))
+    _check("nvfp4_mxfp8_gemm", st)
+    return y
+
+
+def nvfp4_mxfp8_grouped_gemm(a, offsets, b, row_index=None, m_total=None, out=None):
+    """Grouped MXFP8 GEMM: a = (q [a_rows, k], sc [a_rows, k/32]); offsets
+    int32 [groups+1] on the device; b = (q [groups, n, k], sc [groups, n,
+    k/32]); row_index optional int32 [m_total]."""
+    aq, asc = a
+    bq, bsc = b
+    _dev(offsets, "offsets", (torch.int32,), 1)
+    groups, n, k = bq.shape[0], bq.shape[1], bq.shape[2]
+    if m_total is None:
+        m_total = row_index.numel() if row_index is not None else aq.shape[0]
+    y = out if out is not None else torch.empty((m_total, n), dtype=torch.float32, device=aq.device)
+    st = lib().nvfp4_mxfp8_grouped_gemm(_ptr(aq), _ptr(asc), aq.shape[0], _ptr(row_index), m_total,
+                                        _ptr(offsets), groups, _ptr(bq), _ptr(bsc), n, k, _ptr(y),
+                                        _stream(aq.device))
+    _check("nvfp4_mxfp8_grouped_gemm", st)
+    return y
+
+
 def nvfp4_moe_route(logits, topk, out=None):
     """Top-k routing of fp32 logits [tokens, experts] into the contiguous
     per-expert layout on the device.  Returns a dict of int32 tensors:
@@ -312,4 +367,14 @@ def nvfp4_debug_encode_e4m3(v):
     out = torch.empty(v.shape, dtype=torch.uint8, device=v.device)
     _check("nvfp4_debug_encode_e4m3",
            lib().nvfp4_debug_encode_e4m3(_ptr(v), v.numel(), _ptr(out), _stream(v.device)))
+    return out
+
+
+def nvfp4_debug_encode_fp8(v):
+    """E4M3 code (sign | RNE_SAT magnitude) of each float32 in v through the
+    pack-convert the MXFP8 quantizer uses (specified for |v| <= 448)."""
+    _dev(v, "v", (torch.float32,))
+    out = torch.empty(v.shape, dtype=torch.uint8, device=v.device)
+    _check("nvfp4_debug_encode_fp8",
+           lib().nvfp4_debug_encode_fp8(_ptr(v), v.numel(), _ptr(out), _stream(v.device)))
     return out

@@ -8,6 +8,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libnvfp4.so")
 SOURCES = ["abi_common.hip", "quantize.hip", "swiglu_quantize.hip", "route.hip", "dequantize.hip",
+           "mxfp8.hip", "mxfp8_gemm.hip",
            "gemm.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

@@ -37,12 +37,11 @@
 // serves one region.  Grouped GEMMs derive the per-expert m-tile prefix from
 // the device offsets in every block, and ragged expert tiles run only their
 // non-empty 32-row slabs.
-#include "nvfp4_internal.h"
+#include "tile_sched.h"
 
 namespace nvfp4 {
 
 constexpr int BK = 128;          // K elements per stage
-constexpr int MAX_GROUPS = 1024;
 
 struct GemmArgs {
   const uint8_t* a_q;
@@ -50,17 +49,12 @@ struct GemmArgs {
   const float* a_s;
   int64_t a_rows;
   const int32_t* row_index;  // grouped only (nullable)
-  int64_t m_total;           // grouped: output rows; dense: m
-  const int32_t* offsets;    // grouped only
-  int groups;                // grouped only
   const uint8_t* b_q;
   const uint8_t* b_sb;
   const float* b_s;
   int64_t n, k;
   float* y;
-  int tiles_n;
-  int xcd_n;  // XCD regions along N (8 / xcd_n along M), register-direct kernel
-  int slots;  // waves that run at once on one XCD (one per SIMD)
+  TileGrid t;  // output rows / expert offsets and the launch plan
 };
 
 __device__ __forceinline__ f16x2 as_h2(uint32_t v) { return __builtin_bit_cast(f16x2, v); }
@@ -240,109 +234,16 @@ __device__ __forceinline__ void rd_body(const GemmArgs& p, const uint8_t* const*
 template <int TM, int TN, bool FAST>
 __global__ __launch_bounds__(64) void gemm_rd_kernel(GemmArgs p) {
   constexpr int BM = 32 * TM, BN = 32 * TN;
-  constexpr int GPT = MAX_GROUPS / 64;
   __shared__ int32_t s_prefix[MAX_GROUPS + 1];
   __shared__ float s_rowscale[BM];
 
   const int lane = threadIdx.x;
   const int h = lane >> 5, li = lane & 31;
 
-  // ---- block -> XCD region -> tile.  Blocks are dealt round-robin to the
-  // 8 XCDs (block b runs on XCD b % 8); each XCD owns one region of an
-  // (8 / xcd_n) x xcd_n split of the tile grid so its L2 holds that region's
-  // A rows and B columns.  Inside a region, n runs fastest.
-  const int xcd = blockIdx.x % 8;
-  const int64_t jloc = blockIdx.x / 8;
-  const int xn = xcd % p.xcd_n, xm = xcd / p.xcd_n, XM = 8 / p.xcd_n;
-  const int64_t npx = (p.tiles_n + p.xcd_n - 1) / p.xcd_n;
-  const int64_t nlo = xn * npx, nhi = min((int64_t)p.tiles_n, nlo + npx);
-  if (nlo >= nhi) return;  // block-uniform
-  const int64_t width = nhi - nlo;
-  // Region tiles are issued in order; when the last round of a region would
-  // leave more than half of the XCD's wave slots idle, its tiles are issued
-  // as two 64-row halves so that round takes about half as long.
-  auto place = [&](int64_t mcount, int64_t& jf, int& hf) -> bool {
-    const int64_t T = mcount * width;
-    const int64_t tail = T % p.slots;
-    const int64_t split = (tail != 0 && 2 * tail <= p.slots) ? tail : 0;
-    const int64_t F = T - split;
-    if (jloc < F) {
-      jf = jloc;
-      hf = -1;
-      return true;
-    }
-    const int64_t hidx = jloc - F;
-    if (hidx >= 2 * split) return false;
-    jf = F + hidx / 2;
-    hf = (int)(hidx & 1);
-    return true;
-  };
-  int64_t jf = 0, mt, nt;
-  int hf = -1;
-  int64_t row_lo, row_hi;
-  int g = 0;
-  if (p.offsets) {
-    const int G = p.groups;
-    int32_t local = 0;
-    int32_t cnt[GPT];
-#pragma unroll
-    for (int i = 0; i < GPT; ++i) {
-      const int gg = lane * GPT + i;
-      int32_t c = 0;
-      if (gg < G) {
-        int64_t lo = min(max((int64_t)p.offsets[gg], (int64_t)0), p.m_total);
-        int64_t hi = min(max((int64_t)p.offsets[gg + 1], lo), p.m_total);
-        c = (int32_t)((hi - lo + BM - 1) / BM);
-      }
-      cnt[i] = c;
-      local += c;
-    }
-    int32_t incl = local;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-      int32_t o = __shfl_up(incl, d, 64);
-      if (lane >= d) incl += o;
-    }
-    int32_t run = incl - local;
-#pragma unroll
-    for (int i = 0; i < GPT; ++i) {
-      const int gg = lane * GPT + i;
-      if (gg <= G) s_prefix[gg] = run;
-      run += cnt[i];
-    }
-    __syncthreads();
-    const int64_t total_mt = s_prefix[G];
-    const int64_t mpx = (total_mt + XM - 1) / XM;
-    const int64_t mcount = min(mpx, max(total_mt - xm * mpx, (int64_t)0));
-    if (!place(mcount, jf, hf)) return;  // block-uniform
-    mt = xm * mpx + jf / width;
-    nt = nlo + jf % width;
-    int lo = 0, hi = G - 1;
-    while (lo < hi) {
-      int mid = (lo + hi + 1) >> 1;
-      if (s_prefix[mid] <= mt) lo = mid; else hi = mid - 1;
-    }
-    g = lo;
-    const int64_t glo = min(max((int64_t)p.offsets[g], (int64_t)0), p.m_total);
-    const int64_t ghi = min(max((int64_t)p.offsets[g + 1], glo), p.m_total);
-    row_lo = glo + (mt - s_prefix[g]) * BM;
-    row_hi = min(ghi, row_lo + BM);
-  } else {
-    const int64_t tiles_m = (p.m_total + BM - 1) / BM;
-    const int64_t mpx = (tiles_m + XM - 1) / XM;
-    const int64_t mcount = min(mpx, max(tiles_m - xm * mpx, (int64_t)0));
-    if (!place(mcount, jf, hf)) return;  // block-uniform
-    mt = xm * mpx + jf / width;
-    nt = nlo + jf % width;
-    row_lo = mt * BM;
-    row_hi = min(p.m_total, row_lo + BM);
-  }
-  if (hf >= 0) {  // half tile: rows [row_lo + 64 hf, row_lo + 64 hf + 64)
-    row_lo += 64 * hf;
-    row_hi = min(row_hi, row_lo + 64);
-    if (row_lo >= row_hi) return;  // block-uniform
-  }
-  const int64_t n0 = nt * BN;
+  TileRange tr;
+  if (!schedule_tile<BM, BN>(p.t, lane, s_prefix, tr)) return;  // block-uniform
+  const int64_t row_lo = tr.row_lo, row_hi = tr.row_hi, n0 = tr.n0;
+  const int g = tr.g;
   const uint8_t* bq_base = p.b_q + (int64_t)g * p.n * (p.k / 2);
   const uint8_t* bsb_base = p.b_sb + (int64_t)g * p.n * (p.k / 16);
 
@@ -388,37 +289,11 @@ __global__ __launch_bounds__(64) void gemm_rd_kernel(GemmArgs p) {
   }
 }
 
-// Fill of an even split of `tiles` into `parts` ranges (1.0 = balanced).
-static double split_fill(int64_t tiles, int parts) {
-  const int64_t per = (tiles + parts - 1) / parts;
-  return per > 0 ? (double)tiles / (double)(per * parts) : 1.0;
-}
-
 template <int TM, int TN>
-static void launch_gemm_rd(const GemmArgs& a, bool grouped, int64_t groups, hipStream_t stream) {
+static void launch_gemm_rd(const GemmArgs& a, bool grouped, hipStream_t stream) {
   constexpr int BM = 32 * TM, BN = 32 * TN;
   GemmArgs p = a;
-  p.tiles_n = (int)((p.n + BN - 1) / BN);
-  // upper bound on m-tiles (grouped: each group adds at most a partial tile;
-  // the exact count is derived on the device from the offsets)
-  const int64_t tiles_m = (p.m_total + BM - 1) / BM + (grouped ? groups : 0);
-  // XCD split: grouped GEMMs split along M (B changes along M); dense GEMMs
-  // take the split with the best balance, preferring more N regions.
-  p.xcd_n = 1;
-  if (!grouped) {
-    double best = -1.0;
-    for (int xn = 1; xn <= 8; xn *= 2) {
-      const double f = split_fill(tiles_m, 8 / xn) * split_fill(p.tiles_n, xn);
-      if (f >= best) { best = f; p.xcd_n = xn; }
-    }
-  }
-  // one wave per SIMD (the kernel uses the whole register file)
-  p.slots = (nvfp4host::num_cus() / 8) * 4;
-  if (p.slots < 2) p.slots = 2;
-  const int64_t per_xcd = ((tiles_m + (8 / p.xcd_n) - 1) / (8 / p.xcd_n)) *
-                              ((p.tiles_n + p.xcd_n - 1) / p.xcd_n) +
-                          p.slots / 2;  // room for the split tail
-  const int64_t blocks = 8 * per_xcd;
+  const int64_t blocks = plan_tiles<BM, BN>(p.t, p.n, grouped);
   const bool fast = (p.k % BK) == 0 && nvfp4host::aligned(p.a_q, 16) &&
                     nvfp4host::aligned(p.b_q, 16) && nvfp4host::aligned(p.a_sb, 4) &&
                     nvfp4host::aligned(p.b_sb, 4);
@@ -460,9 +335,9 @@ extern "C" int nvfp4_gemm(const uint8_t* a_q, const uint8_t* a_sb, const float* 
   }
   nvfp4::GemmArgs p{};
   p.a_q = a_q; p.a_sb = a_sb; p.a_s = a_s; p.a_rows = m;
-  p.row_index = nullptr; p.m_total = m; p.offsets = nullptr; p.groups = 1;
+  p.row_index = nullptr; p.t.m_total = m; p.t.offsets = nullptr; p.t.groups = 1;
   p.b_q = b_q; p.b_sb = b_sb; p.b_s = b_s; p.n = n; p.k = k; p.y = y;
-  nvfp4::launch_gemm_rd<4, 4>(p, false, 1, str);
+  nvfp4::launch_gemm_rd<4, 4>(p, false, str);
   return nvfp4host::launch_status();
 }
 
@@ -490,10 +365,10 @@ extern "C" int nvfp4_grouped_gemm(const uint8_t* a_q, const uint8_t* a_sb, const
   hipStream_t str = (hipStream_t)stream;
   nvfp4::GemmArgs p{};
   p.a_q = a_q; p.a_sb = a_sb; p.a_s = a_s; p.a_rows = a_rows;
-  p.row_index = row_index; p.m_total = m_total; p.offsets = offsets; p.groups = (int)groups;
+  p.row_index = row_index; p.t.m_total = m_total; p.t.offsets = offsets; p.t.groups = (int)groups;
   p.b_q = b_q; p.b_sb = b_sb; p.b_s = b_s; p.n = n; p.k = k; p.y = y;
   // k == 0 needs no special case: the K loop is empty and the epilogue writes
   // zeros to exactly the rows the groups own
-  nvfp4::launch_gemm_rd<4, 4>(p, true, groups, str);
+  nvfp4::launch_gemm_rd<4, 4>(p, true, str);
   return nvfp4host::launch_status();
 }

@@ -15,6 +15,30 @@ typedef __fp16 hp16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
+typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// streaming 16-byte load (each input byte is read exactly once)
+__device__ __forceinline__ uint4 ld_stream(const uint4* p) {
+  u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+// max of the 16 bf16 magnitudes held in two uint4 (as bf16 bit patterns)
+__device__ __forceinline__ uint32_t block_amax_bits(const uint4& a, const uint4& b) {
+  const uint32_t M = 0x7FFF7FFFu;
+  u16x2 w[8];
+  uint32_t t[8] = {a.x & M, a.y & M, a.z & M, a.w & M, b.x & M, b.y & M, b.z & M, b.w & M};
+#pragma unroll
+  for (int i = 0; i < 8; ++i) w[i] = __builtin_bit_cast(u16x2, t[i]);
+  u16x2 m0 = __builtin_elementwise_max(__builtin_elementwise_max(w[0], w[1]),
+                                       __builtin_elementwise_max(w[2], w[3]));
+  u16x2 m1 = __builtin_elementwise_max(__builtin_elementwise_max(w[4], w[5]),
+                                       __builtin_elementwise_max(w[6], w[7]));
+  u16x2 m = __builtin_elementwise_max(m0, m1);
+  return max((uint32_t)m.x, (uint32_t)m.y);
+}
+
 // ------------------------------------------------------------ E4M3 codec --
 // RNE_SAT onto E4M3 (OCP FN, bias 7, max 448) for v >= 0 or +inf.  Values at
 // or above 448 saturate; below 2^-6 the grid is the subnormal step 2^-9 and

@@ -30,30 +30,6 @@ enum QuantMode { MODE_ROW = 0, MODE_AMAX_IN = 1, MODE_GROUP = 2 };
 #define NVFP4_Q_WAVES_PER_SIMD 8
 #endif
 
-typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-
-// streaming 16-byte load (each input byte is read exactly once)
-__device__ __forceinline__ uint4 ld_stream(const uint4* p) {
-  u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
-  return make_uint4(v.x, v.y, v.z, v.w);
-}
-
-// max of the 16 bf16 magnitudes held in two uint4 (as bf16 bit patterns)
-__device__ __forceinline__ uint32_t block_amax_bits(const uint4& a, const uint4& b) {
-  const uint32_t M = 0x7FFF7FFFu;
-  u16x2 w[8];
-  uint32_t t[8] = {a.x & M, a.y & M, a.z & M, a.w & M, b.x & M, b.y & M, b.z & M, b.w & M};
-#pragma unroll
-  for (int i = 0; i < 8; ++i) w[i] = __builtin_bit_cast(u16x2, t[i]);
-  u16x2 m0 = __builtin_elementwise_max(__builtin_elementwise_max(w[0], w[1]),
-                                       __builtin_elementwise_max(w[2], w[3]));
-  u16x2 m1 = __builtin_elementwise_max(__builtin_elementwise_max(w[4], w[5]),
-                                       __builtin_elementwise_max(w[6], w[7]));
-  u16x2 m = __builtin_elementwise_max(m0, m1);
-  return max((uint32_t)m.x, (uint32_t)m.y);
-}
-
 __device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 

@@ -1,0 +1,171 @@
+// tile_sched.h -- block -> output-tile mapping shared by the GEMM kernels
+// (dense and grouped, gfx950): XCD-aware regions, device-side expert tile
+// prefix from the offsets, and the split of a region's last partial round.
+#pragma once
+
+#include "nvfp4_internal.h"
+
+namespace nvfp4 {
+
+constexpr int MAX_GROUPS = 1024;
+
+// What the mapping needs: the output rows (dense) or the device offsets of a
+// contiguous per-expert layout (grouped), and the host's launch plan.
+struct TileGrid {
+  int64_t m_total;          // grouped: output rows; dense: m
+  const int32_t* offsets;   // grouped only (nullptr: dense)
+  int groups;               // grouped only
+  int tiles_n;
+  int xcd_n;  // XCD regions along N (8 / xcd_n along M)
+  int slots;  // waves that run at once on one XCD (one per SIMD)
+};
+
+// The block's output tile: rows [row_lo, row_hi) of expert g (0 when dense),
+// columns from n0.
+struct TileRange {
+  int64_t row_lo, row_hi, n0;
+  int g;
+};
+
+// Blocks are dealt round-robin to the 8 XCDs (block b runs on XCD b % 8);
+// each XCD owns one region of an (8 / xcd_n) x xcd_n split of the tile grid
+// so its L2 holds that region's A rows and B columns.  Inside a region, n runs
+// fastest.  Grouped: every block derives the per-expert m-tile prefix from the
+// device offsets (a wave scan into s_prefix) and binary-searches its expert.
+// Returns false when the block has no tile (block-uniform).  Called by the
+// whole block (one wave of 64 lanes).
+template <int BM, int BN>
+__device__ __forceinline__ bool schedule_tile(const TileGrid& t, int lane, int32_t* s_prefix,
+                                              TileRange& out) {
+  constexpr int GPT = MAX_GROUPS / 64;
+  const int xcd = blockIdx.x % 8;
+  const int64_t jloc = blockIdx.x / 8;
+  const int xn = xcd % t.xcd_n, xm = xcd / t.xcd_n, XM = 8 / t.xcd_n;
+  const int64_t npx = (t.tiles_n + t.xcd_n - 1) / t.xcd_n;
+  const int64_t nlo = xn * npx, nhi = min((int64_t)t.tiles_n, nlo + npx);
+  if (nlo >= nhi) return false;  // block-uniform
+  const int64_t width = nhi - nlo;
+  // Region tiles are issued in order; when the last round of a region would
+  // leave more than half of the XCD's wave slots idle, its tiles are issued
+  // as two 64-row halves so that round takes about half as long.
+  auto place = [&](int64_t mcount, int64_t& jf, int& hf) -> bool {
+    const int64_t T = mcount * width;
+    const int64_t tail = T % t.slots;
+    const int64_t split = (tail != 0 && 2 * tail <= t.slots) ? tail : 0;
+    const int64_t F = T - split;
+    if (jloc < F) {
+      jf = jloc;
+      hf = -1;
+      return true;
+    }
+    const int64_t hidx = jloc - F;
+    if (hidx >= 2 * split) return false;
+    jf = F + hidx / 2;
+    hf = (int)(hidx & 1);
+    return true;
+  };
+  int64_t jf = 0, mt, nt;
+  int hf = -1;
+  int64_t row_lo, row_hi;
+  int g = 0;
+  if (t.offsets) {
+    const int G = t.groups;
+    int32_t local = 0;
+    int32_t cnt[GPT];
+#pragma unroll
+    for (int i = 0; i < GPT; ++i) {
+      const int gg = lane * GPT + i;
+      int32_t c = 0;
+      if (gg < G) {
+        int64_t lo = min(max((int64_t)t.offsets[gg], (int64_t)0), t.m_total);
+        int64_t hi = min(max((int64_t)t.offsets[gg + 1], lo), t.m_total);
+        c = (int32_t)((hi - lo + BM - 1) / BM);
+      }
+      cnt[i] = c;
+      local += c;
+    }
+    int32_t incl = local;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      int32_t o = __shfl_up(incl, d, 64);
+      if (lane >= d) incl += o;
+    }
+    int32_t run = incl - local;
+#pragma unroll
+    for (int i = 0; i < GPT; ++i) {
+      const int gg = lane * GPT + i;
+      if (gg <= G) s_prefix[gg] = run;
+      run += cnt[i];
+    }
+    __syncthreads();
+    const int64_t total_mt = s_prefix[G];
+    const int64_t mpx = (total_mt + XM - 1) / XM;
+    const int64_t mcount = min(mpx, max(total_mt - xm * mpx, (int64_t)0));
+    if (!place(mcount, jf, hf)) return false;  // block-uniform
+    mt = xm * mpx + jf / width;
+    nt = nlo + jf % width;
+    int lo = 0, hi = G - 1;
+    while (lo < hi) {
+      int mid = (lo + hi + 1) >> 1;
+      if (s_prefix[mid] <= mt) lo = mid; else hi = mid - 1;
+    }
+    g = lo;
+    const int64_t glo = min(max((int64_t)t.offsets[g], (int64_t)0), t.m_total);
+    const int64_t ghi = min(max((int64_t)t.offsets[g + 1], glo), t.m_total);
+    row_lo = glo + (mt - s_prefix[g]) * BM;
+    row_hi = min(ghi, row_lo + BM);
+  } else {
+    const int64_t tiles_m = (t.m_total + BM - 1) / BM;
+    const int64_t mpx = (tiles_m + XM - 1) / XM;
+    const int64_t mcount = min(mpx, max(tiles_m - xm * mpx, (int64_t)0));
+    if (!place(mcount, jf, hf)) return false;  // block-uniform
+    mt = xm * mpx + jf / width;
+    nt = nlo + jf % width;
+    row_lo = mt * BM;
+    row_hi = min(t.m_total, row_lo + BM);
+  }
+  if (hf >= 0) {  // half tile: rows [row_lo + 64 hf, row_lo + 64 hf + 64)
+    row_lo += 64 * hf;
+    row_hi = min(row_hi, row_lo + 64);
+    if (row_lo >= row_hi) return false;  // block-uniform
+  }
+  out.row_lo = row_lo;
+  out.row_hi = row_hi;
+  out.n0 = nt * BN;
+  out.g = g;
+  return true;
+}
+
+// Fill of an even split of `tiles` into `parts` ranges (1.0 = balanced).
+static inline double split_fill(int64_t tiles, int parts) {
+  const int64_t per = (tiles + parts - 1) / parts;
+  return per > 0 ? (double)tiles / (double)(per * parts) : 1.0;
+}
+
+// Host launch plan for BM x BN tiles with one wave per SIMD: fills tiles_n,
+// xcd_n and slots and returns the number of one-wave blocks to launch.
+template <int BM, int BN>
+static int64_t plan_tiles(TileGrid& t, int64_t n, bool grouped) {
+  t.tiles_n = (int)((n + BN - 1) / BN);
+  // upper bound on m-tiles (grouped: each group adds at most a partial tile;
+  // the exact count is derived on the device from the offsets)
+  const int64_t tiles_m = (t.m_total + BM - 1) / BM + (grouped ? t.groups : 0);
+  // XCD split: grouped GEMMs split along M (B changes along M); dense GEMMs
+  // take the split with the best balance, preferring more N regions.
+  t.xcd_n = 1;
+  if (!grouped) {
+    double best = -1.0;
+    for (int xn = 1; xn <= 8; xn *= 2) {
+      const double f = split_fill(tiles_m, 8 / xn) * split_fill(t.tiles_n, xn);
+      if (f >= best) { best = f; t.xcd_n = xn; }
+    }
+  }
+  t.slots = (nvfp4host::num_cus() / 8) * 4;
+  if (t.slots < 2) t.slots = 2;
+  const int64_t per_xcd = ((tiles_m + (8 / t.xcd_n) - 1) / (8 / t.xcd_n)) *
+                              ((t.tiles_n + t.xcd_n - 1) / t.xcd_n) +
+                          t.slots / 2;  // room for the split tail
+  return 8 * per_xcd;
+}
+
+}  // namespace nvfp4
