@@ -20,12 +20,12 @@ run of the same K steps with HIP events recorded on the launch stream around
 every launch; each kernel's achieved GB/s or TFLOP/s is its algorithmic bytes
 or flops (stated in the design notes) over that duration.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-next]
 Prints one JSON line on stdout; progress goes to stderr.
 
 Traffic counters (profiles/traffic.json, used for roofline.traffic):
   rocprofv3 --pmc FETCH_SIZE (then WRITE_SIZE) --output-format csv -d DIR -- \
-      python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline
+      python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline --no-next
   the same two counters over `python3 bench.py --calib-copy` (a plain 1 GiB
   device copy), then
   python bench.py --pmc-summary FETCH_DIR WRITE_DIR CALIB_FETCH_DIR CALIB_WRITE_DIR
@@ -52,10 +52,23 @@ def log(*a):
 T0 = time.time()
 
 
-def csrc_digest():
+# Source files each timed kernel is built from (its traffic counters stay
+# valid until one of these changes).
+_QUANT_SRC = ("quantize.hip", "nvfp4_internal.h", "abi_common.hip")
+_GEMM_SRC = ("gemm.hip", "tile_sched.h", "nvfp4_internal.h", "abi_common.hip")
+KERNEL_SOURCES = {
+    "quantize_weight_dense": _QUANT_SRC, "quantize_weight_up": _QUANT_SRC,
+    "quantize_weight_down": _QUANT_SRC, "quantize_rows_dense": _QUANT_SRC,
+    "quantize_rows_moe": _QUANT_SRC, "requantize_rows_amax_reuse": _QUANT_SRC,
+    "gemm_dense": _GEMM_SRC, "grouped_gemm_up": _GEMM_SRC, "grouped_gemm_down": _GEMM_SRC,
+}
+
+
+def kernel_digest(name):
+    """Digest of the source files kernel `name` is built from."""
     h = hashlib.sha256()
     d = os.path.join(ROOT, "nvfp4_token_quantization_amd", "csrc")
-    for f in sorted(os.listdir(d)):
+    for f in sorted(KERNEL_SOURCES[name]):
         h.update(f.encode())
         h.update(open(os.path.join(d, f), "rb").read())
     return h.hexdigest()[:16]
@@ -124,7 +137,7 @@ def pmc_summary(fetch_dir, write_dir, cfetch_dir, cwrite_dir):
     """Per-launch HBM bytes of every step launch from FETCH_SIZE and
     WRITE_SIZE runs of this bench, each scaled by the same counter's reading
     for a plain copy of CALIB_BYTES; writes profiles/traffic.json."""
-    out = {"csrc_digest": csrc_digest(), "calibration": {}, "kernels": {}}
+    out = {"calibration": {}, "kernels": {}}
     per = {}
     for counter, ddir, cdir in (("FETCH_SIZE", fetch_dir, cfetch_dir),
                                 ("WRITE_SIZE", write_dir, cwrite_dir)):
@@ -133,7 +146,8 @@ def pmc_summary(fetch_dir, write_dir, cfetch_dir, cwrite_dir):
         factor = (CALIB_BYTES / 1024.0) / big[3]
         out["calibration"][counter] = {"copy_kernel": big[1], "copy_bytes": CALIB_BYTES,
                                        "counter_KiB": big[3], "factor": factor}
-        disp = [d for d in _pmc_dispatches(ddir, counter) if "nvfp4" in d[1]]
+        # the step's launches (the MoE layout is routed once, before the steps)
+        disp = [d for d in _pmc_dispatches(ddir, counter) if "nvfp4" in d[1] and "route_" not in d[1]]
         n_per_step = sum(c for _, c in STEP_LAUNCHES)
         steps = len(disp) // n_per_step
         if steps * n_per_step != len(disp):
@@ -149,7 +163,7 @@ def pmc_summary(fetch_dir, write_dir, cfetch_dir, cwrite_dir):
         f = sum(d["FETCH_SIZE"]) / len(d["FETCH_SIZE"])
         w = sum(d["WRITE_SIZE"]) / len(d["WRITE_SIZE"])
         out["kernels"][name] = {"fetch_bytes": round(f), "write_bytes": round(w),
-                                "bytes_per_launch": round(f + w)}
+                                "bytes_per_launch": round(f + w), "source_digest": kernel_digest(name)}
     path = os.path.join(ROOT, "profiles", "traffic.json")
     json.dump(out, open(path, "w"), indent=1)
     print(json.dumps(out, indent=1))
@@ -165,6 +179,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-next", action="store_true",
+                    help="skip the separately timed rows (used by the counter runs)")
     ap.add_argument("--cpu-sample-rows", type=int, default=4096)
     ap.add_argument("--cpu-sample-entries", type=int, default=30000000)
     args = ap.parse_args()
@@ -360,66 +376,67 @@ def main():
         torch.cuda.synchronize()
         return a.elapsed_time(b) / iters
 
-    # SwiGLU -> per-token requantize chained on the step's own up-GEMM output
-    # (fused gate|up, 32768 x 1536 fp32 -> H 32768 x 768 quantized in place)
-    FH = N3 // 2
-    sw = (empty((MR, FH // 2), u8), empty((MR, FH // 16), u8), empty((MR,), f32), empty((MR,), f32))
-    ms = time_extra(lambda: L.nvfp4_swiglu_quantize_rows(
-        p(out["y3"]), MR, FH, None, p(sw[3]), p(sw[0]), p(sw[1]), p(sw[2]), sp), K)
-    byt = MR * N3 * 4 + MR * FH // 2 + MR * FH // 16 + 2 * MR * 4
-    nxt["swiglu_quantize_chained"] = {"ms": round(ms, 4), "GB/s": round(byt / ms / 1e6, 1),
-                                      "frac_hbm": round(byt / ms / 1e6 / HBM_PEAK_GBS, 4),
-                                      "bytes": int(byt)}
-    # on-device routing of the MoE batch (4096 tokens x 128 logits -> top-8
-    # contiguous layout: experts, offsets, row_index, slot_of)
-    rbuf = {k: torch.empty_like(v) for k, v in rt3.items()}
-    TT, EE = logits3.shape
-    ms = time_extra(lambda: L.nvfp4_moe_route(
-        p(logits3), TT, EE, 8, p(rbuf["experts"]), p(rbuf["offsets"]), p(rbuf["row_index"]),
-        p(rbuf["slot_of"]), sp), K)
-    byt = TT * EE * 4 + 4 * (3 * TT * 8 + EE + 1) + 4 * TT * 8
-    nxt["moe_route"] = {"ms": round(ms, 4), "GB/s": round(byt / ms / 1e6, 1),
-                        "frac_hbm": round(byt / ms / 1e6 / HBM_PEAK_GBS, 4), "bytes": int(byt),
-                        "tokens_per_s": round(TT / ms * 1e3, 1)}
-    # bf16 dequantization of forward operands for a dequantized backward:
-    # the MoE down input H (per-token scales) and the fused W_up (per expert)
-    for name, (qq, ss, rows, kk, rps) in (
-            ("dequantize_rows_h", (out["h4"], out["h4"][2], MH, K4, 1)),
-            ("dequantize_weight_up", (out["w3"], out["w3"][2], E * N3, K3, N3))):
-        dq = empty((rows, kk), torch.bfloat16)
-        ms = time_extra(lambda: L.nvfp4_dequantize_rows(
-            p(qq[0]), p(qq[1]), p(ss), rows, kk, rps, p(dq), sp), K)
-        byt = rows * kk // 2 + rows * kk // 16 + (rows // rps) * 4 + rows * kk * 2
-        nxt[name] = {"ms": round(ms, 4), "GB/s": round(byt / ms / 1e6, 1),
-                     "frac_hbm": round(byt / ms / 1e6 / HBM_PEAK_GBS, 4), "bytes": int(byt)}
-        del dq
-    # MXFP8 variant: quantize the dense activation, then the dense and the
-    # grouped up-projection GEMMs on the scaled fp8 MFMA
-    mx_x2 = (empty((M2, K2), u8), empty((M2, K2 // 32), u8))
-    mx_w2 = (empty((N2, K2), u8), empty((N2, K2 // 32), u8))
-    mx_x3 = (empty((T3, K3), u8), empty((T3, K3 // 32), u8))
-    mx_w3 = (empty((E * N3, K3), u8), empty((E * N3, K3 // 32), u8))
-    for src, dst, rows, kk in ((W2, mx_w2, N2, K2), (X3[0], mx_x3, T3, K3), (W3, mx_w3, E * N3, K3)):
-        st = L.nvfp4_mxfp8_quantize_rows(p(src), rows, kk, p(dst[0]), p(dst[1]), sp)
-        if st != 0:
-            raise RuntimeError("mxfp8 quantize failed: %s" % nv.status_string(st))
-    ms = time_extra(lambda: L.nvfp4_mxfp8_quantize_rows(p(X2[0]), M2, K2, p(mx_x2[0]), p(mx_x2[1]), sp), K)
-    byt = M2 * K2 * 2 + M2 * K2 + M2 * K2 // 32
-    nxt["mxfp8_quantize_rows_dense"] = {"ms": round(ms, 4), "GB/s": round(byt / ms / 1e6, 1),
-                                        "frac_hbm": round(byt / ms / 1e6 / HBM_PEAK_GBS, 4), "bytes": int(byt)}
-    ms = time_extra(lambda: L.nvfp4_mxfp8_gemm(p(mx_x2[0]), p(mx_x2[1]), M2, p(mx_w2[0]), p(mx_w2[1]),
-                                               N2, K2, p(out["y2"]), sp), K)
-    fl = 2.0 * M2 * N2 * K2
-    nxt["mxfp8_gemm_dense"] = {"ms": round(ms, 4), "TFLOP/s": round(fl / ms / 1e9, 1),
-                               "frac_mfma_fp8": round(fl / ms / 1e9 / MFMA_FP8_PEAK_TFS, 4), "flop": fl}
-    ms = time_extra(lambda: L.nvfp4_mxfp8_grouped_gemm(
-        p(mx_x3[0]), p(mx_x3[1]), T3, p(row_index), MR, p(offsets), E, p(mx_w3[0]), p(mx_w3[1]),
-        N3, K3, p(out["y3"]), sp), K)
-    fl = 2.0 * MR * N3 * K3
-    nxt["mxfp8_grouped_gemm_up"] = {"ms": round(ms, 4), "TFLOP/s": round(fl / ms / 1e9, 1),
-                                    "frac_mfma_fp8": round(fl / ms / 1e9 / MFMA_FP8_PEAK_TFS, 4), "flop": fl}
-    del mx_x2, mx_w2, mx_x3, mx_w3
-    log("next rows: %s" % nxt)
+    if not args.no_next:
+        # SwiGLU -> per-token requantize chained on the step's own up-GEMM output
+        # (fused gate|up, 32768 x 1536 fp32 -> H 32768 x 768 quantized in place)
+        FH = N3 // 2
+        sw = (empty((MR, FH // 2), u8), empty((MR, FH // 16), u8), empty((MR,), f32), empty((MR,), f32))
+        ms = time_extra(lambda: L.nvfp4_swiglu_quantize_rows(
+            p(out["y3"]), MR, FH, None, p(sw[3]), p(sw[0]), p(sw[1]), p(sw[2]), sp), K)
+        byt = MR * N3 * 4 + MR * FH // 2 + MR * FH // 16 + 2 * MR * 4
+        nxt["swiglu_quantize_chained"] = {"ms": round(ms, 4), "GB/s": round(byt / ms / 1e6, 1),
+                                          "frac_hbm": round(byt / ms / 1e6 / HBM_PEAK_GBS, 4),
+                                          "bytes": int(byt)}
+        # on-device routing of the MoE batch (4096 tokens x 128 logits -> top-8
+        # contiguous layout: experts, offsets, row_index, slot_of)
+        rbuf = {k: torch.empty_like(v) for k, v in rt3.items()}
+        TT, EE = logits3.shape
+        ms = time_extra(lambda: L.nvfp4_moe_route(
+            p(logits3), TT, EE, 8, p(rbuf["experts"]), p(rbuf["offsets"]), p(rbuf["row_index"]),
+            p(rbuf["slot_of"]), sp), K)
+        byt = TT * EE * 4 + 4 * (3 * TT * 8 + EE + 1) + 4 * TT * 8
+        nxt["moe_route"] = {"ms": round(ms, 4), "GB/s": round(byt / ms / 1e6, 1),
+                            "frac_hbm": round(byt / ms / 1e6 / HBM_PEAK_GBS, 4), "bytes": int(byt),
+                            "tokens_per_s": round(TT / ms * 1e3, 1)}
+        # bf16 dequantization of forward operands for a dequantized backward:
+        # the MoE down input H (per-token scales) and the fused W_up (per expert)
+        for name, (qq, ss, rows, kk, rps) in (
+                ("dequantize_rows_h", (out["h4"], out["h4"][2], MH, K4, 1)),
+                ("dequantize_weight_up", (out["w3"], out["w3"][2], E * N3, K3, N3))):
+            dq = empty((rows, kk), torch.bfloat16)
+            ms = time_extra(lambda: L.nvfp4_dequantize_rows(
+                p(qq[0]), p(qq[1]), p(ss), rows, kk, rps, p(dq), sp), K)
+            byt = rows * kk // 2 + rows * kk // 16 + (rows // rps) * 4 + rows * kk * 2
+            nxt[name] = {"ms": round(ms, 4), "GB/s": round(byt / ms / 1e6, 1),
+                         "frac_hbm": round(byt / ms / 1e6 / HBM_PEAK_GBS, 4), "bytes": int(byt)}
+            del dq
+        # MXFP8 variant: quantize the dense activation, then the dense and the
+        # grouped up-projection GEMMs on the scaled fp8 MFMA
+        mx_x2 = (empty((M2, K2), u8), empty((M2, K2 // 32), u8))
+        mx_w2 = (empty((N2, K2), u8), empty((N2, K2 // 32), u8))
+        mx_x3 = (empty((T3, K3), u8), empty((T3, K3 // 32), u8))
+        mx_w3 = (empty((E * N3, K3), u8), empty((E * N3, K3 // 32), u8))
+        for src, dst, rows, kk in ((W2, mx_w2, N2, K2), (X3[0], mx_x3, T3, K3), (W3, mx_w3, E * N3, K3)):
+            st = L.nvfp4_mxfp8_quantize_rows(p(src), rows, kk, p(dst[0]), p(dst[1]), sp)
+            if st != 0:
+                raise RuntimeError("mxfp8 quantize failed: %s" % nv.status_string(st))
+        ms = time_extra(lambda: L.nvfp4_mxfp8_quantize_rows(p(X2[0]), M2, K2, p(mx_x2[0]), p(mx_x2[1]), sp), K)
+        byt = M2 * K2 * 2 + M2 * K2 + M2 * K2 // 32
+        nxt["mxfp8_quantize_rows_dense"] = {"ms": round(ms, 4), "GB/s": round(byt / ms / 1e6, 1),
+                                            "frac_hbm": round(byt / ms / 1e6 / HBM_PEAK_GBS, 4), "bytes": int(byt)}
+        ms = time_extra(lambda: L.nvfp4_mxfp8_gemm(p(mx_x2[0]), p(mx_x2[1]), M2, p(mx_w2[0]), p(mx_w2[1]),
+                                                   N2, K2, p(out["y2"]), sp), K)
+        fl = 2.0 * M2 * N2 * K2
+        nxt["mxfp8_gemm_dense"] = {"ms": round(ms, 4), "TFLOP/s": round(fl / ms / 1e9, 1),
+                                   "frac_mfma_fp8": round(fl / ms / 1e9 / MFMA_FP8_PEAK_TFS, 4), "flop": fl}
+        ms = time_extra(lambda: L.nvfp4_mxfp8_grouped_gemm(
+            p(mx_x3[0]), p(mx_x3[1]), T3, p(row_index), MR, p(offsets), E, p(mx_w3[0]), p(mx_w3[1]),
+            N3, K3, p(out["y3"]), sp), K)
+        fl = 2.0 * MR * N3 * K3
+        nxt["mxfp8_grouped_gemm_up"] = {"ms": round(ms, 4), "TFLOP/s": round(fl / ms / 1e9, 1),
+                                        "frac_mfma_fp8": round(fl / ms / 1e9 / MFMA_FP8_PEAK_TFS, 4), "flop": fl}
+        del mx_x2, mx_w2, mx_x3, mx_w3
+        log("next rows: %s" % nxt)
 
     # dominant kernel = longest per step
     dom = max(names, key=lambda n: per_kernel_ms[n])
@@ -440,7 +457,7 @@ def main():
         try:
             tr = json.load(open(tfile))
             ent = tr.get("kernels", {}).get(dom)
-            if ent and tr.get("csrc_digest") == csrc_digest():
+            if ent and ent.get("source_digest") == kernel_digest(dom):
                 roof["traffic"] = ent["bytes_per_launch"]
         except (ValueError, KeyError):
             pass
