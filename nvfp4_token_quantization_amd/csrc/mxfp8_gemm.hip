@@ -12,18 +12,18 @@
 // byte stands for inside a block does not matter as long as A and B agree,
 // so lane (li, h) simply reads bytes [32 b + 16 h, +16) of each block b.
 //
-// Tiling follows the NVFP4 kernel (register-direct, one wave per block, a
-// 128 x 128 tile of 4 x 4 MFMA tiles with 256 fp32 accumulators, operands
-// loaded from L2 one K stage of 64 ahead into a register double buffer, the
-// XCD-aware tile order of tile_sched.h), without any decode: the E4M3 bytes
-// and E8M0 codes go to the MFMA as they are stored.
+// There is no decode, so the kernel is bound by getting operands to the
+// MFMAs: four waves share a 256 x 256 block tile through LDS (below) and the
+// XCD-aware tile order of tile_sched.h keeps a region's panels in one L2.
+// Measured on the 4096 x 9728 x 2560 shape: with operand loads removed the
+// MFMAs and LDS traffic alone take 137 us; a first version whose loads were
+// each waited for before the next was issued (a mask applied right after the
+// load) ran 309 us, so masks are applied only when the data reaches LDS.
 #include "tile_sched.h"
 
 namespace nvfp4 {
 
 typedef int i32x8 __attribute__((ext_vector_type(8)));
-
-constexpr int MX_BK = 64;  // K elements per stage (one MFMA K step, two blocks)
 
 struct MxGemmArgs {
   const uint8_t* a_q;
@@ -37,64 +37,10 @@ struct MxGemmArgs {
   TileGrid t;
 };
 
-template <int TM, int TN>
-struct MxStage {
-  uint4 a[TM][2];
-  uint4 b[TN][2];
-  uint32_t as[TM];
-  uint32_t bs[TN];
-};
-
-// 16 bytes [off, off + 16) of a row holding `valid` bytes (bytes past the
-// end read as zero and are not fetched)
-__device__ __forceinline__ uint4 mx_load16(const uint8_t* row, int64_t off, int64_t valid,
-                                           bool fast) {
-  if (fast || off + 16 <= valid) return *reinterpret_cast<const uint4*>(row + off);
-  if (off >= valid) return make_uint4(0, 0, 0, 0);
-  uint32_t v[4] = {0u, 0u, 0u, 0u};
-  for (int i = 0; i < 16; ++i)
-    if (off + i < valid) v[i >> 2] |= (uint32_t)row[off + i] << (8 * (i & 3));
-  return make_uint4(v[0], v[1], v[2], v[3]);
-}
-
-// Operand rows are kept as 32-bit row numbers (the register file is full):
-// rows outside the operand (ragged tiles, bad row indices) use row 0 of B,
-// which exists whenever there is K work, so every load is in bounds and
-// branch-free; a clear mask bit replaces their data by zeros (scale 2^0).
-template <int TM, int TN, int VS, bool FAST>
-__device__ __forceinline__ void mx_load(const MxGemmArgs& p, const uint8_t* aq, const uint8_t* asc,
-                                        const uint32_t* arow, uint32_t amask, const uint8_t* bq,
-                                        const uint8_t* bsc, const uint32_t* brow, uint32_t bmask,
-                                        int h, int64_t k0, MxStage<TM, TN>& r) {
-  const int64_t nblk = p.k / 32;
-  const int64_t blk = k0 / 32 + h;  // the block whose scale this lane supplies
-  const bool blk_ok = FAST || blk < nblk;
-  const int64_t o0 = k0 + 16 * h, o1 = k0 + 32 + 16 * h;
-  const uint4 z = make_uint4(0, 0, 0, 0);
-#pragma unroll
-  for (int i = 0; i < VS; ++i) {
-    const bool ok = (amask >> i) & 1u;
-    const uint8_t* rq = (ok ? aq : p.b_q) + (int64_t)arow[i] * p.k;
-    const uint8_t* rs = (ok ? asc : p.b_sc) + (int64_t)arow[i] * nblk;
-    const uint4 x0 = mx_load16(rq, o0, p.k, FAST);
-    const uint4 x1 = mx_load16(rq, o1, p.k, FAST);
-    const uint32_t sc = blk_ok ? (uint32_t)rs[blk_ok ? blk : 0] : 127u;
-    r.a[i][0] = ok ? x0 : z;
-    r.a[i][1] = ok ? x1 : z;
-    r.as[i] = ok ? sc : 127u;
-  }
-#pragma unroll
-  for (int j = 0; j < TN; ++j) {
-    const bool ok = (bmask >> j) & 1u;
-    const uint8_t* rq = (ok ? bq : p.b_q) + (int64_t)brow[j] * p.k;
-    const uint8_t* rs = (ok ? bsc : p.b_sc) + (int64_t)brow[j] * nblk;
-    const uint4 x0 = mx_load16(rq, o0, p.k, FAST);
-    const uint4 x1 = mx_load16(rq, o1, p.k, FAST);
-    const uint32_t sc = blk_ok ? (uint32_t)rs[blk_ok ? blk : 0] : 127u;
-    r.b[j][0] = ok ? x0 : z;
-    r.b[j][1] = ok ? x1 : z;
-    r.bs[j] = ok ? sc : 127u;
-  }
+// v if ok, else zeros (component-wise, so no aggregate select is formed)
+__device__ __forceinline__ uint4 keep_if(bool ok, const uint4& v) {
+  const uint32_t m = ok ? 0xFFFFFFFFu : 0u;
+  return make_uint4(v.x & m, v.y & m, v.z & m, v.w & m);
 }
 
 __device__ __forceinline__ i32x8 mx_operand(const uint4& lo, const uint4& hi) {
@@ -102,106 +48,194 @@ __device__ __forceinline__ i32x8 mx_operand(const uint4& lo, const uint4& hi) {
                  (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
 }
 
-template <int TM, int TN, int VS>
-__device__ __forceinline__ void mx_compute(const MxStage<TM, TN>& r, f32x16 (&acc)[TM][TN]) {
-  i32x8 fa[TM], fb[TN];
+// Four E8M0 codes of blocks [b, b + 4) of a scale row of nblk codes; blocks
+// past the row read as 127 (2^0; their data is zero).  FULL: nblk % 4 == 0,
+// one aligned dword.
+template <bool FULL>
+__device__ __forceinline__ uint32_t mx_scales4(const uint8_t* row, int64_t b, int64_t nblk) {
+  if (FULL) return *reinterpret_cast<const uint32_t*>(row + b);
+  uint32_t v = 0u;
 #pragma unroll
-  for (int i = 0; i < VS; ++i) fa[i] = mx_operand(r.a[i][0], r.a[i][1]);
-#pragma unroll
-  for (int j = 0; j < TN; ++j) fb[j] = mx_operand(r.b[j][0], r.b[j][1]);
-#pragma unroll
-  for (int i = 0; i < VS; ++i)
-#pragma unroll
-    for (int j = 0; j < TN; ++j)
-      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-          fa[i], fb[j], acc[i][j], 0, 0, 0, (int)r.as[i], 0, (int)r.bs[j]);
+  for (int i = 0; i < 4; ++i) v |= (b + i < nblk ? (uint32_t)row[b + i] : 127u) << (8 * i);
+  return v;
 }
 
-template <int TM, int TN, int VS, bool FAST>
-__device__ __forceinline__ void mx_body(const MxGemmArgs& p, const uint8_t* bq,
-                                        const uint8_t* bsc, const uint32_t* arow, uint32_t amask,
-                                        const uint32_t* brow, uint32_t bmask, int h, int li,
-                                        int64_t row_lo, int64_t row_hi, int64_t n0) {
-  f32x16 acc[TM][TN];
+constexpr int MXL_BM = 256, MXL_BN = 256, MXL_BK = 128;
+
+__device__ __forceinline__ int mxl_swz(int r) { return ((r >> 1) & 7) ^ ((r & 1) << 2); }
+
+template <bool FULL>
+__global__ __launch_bounds__(256) void mxfp8_gemm_lds_kernel(MxGemmArgs p) {
+  __shared__ int32_t s_prefix[MAX_GROUPS + 1];
+  __shared__ uint4 s_a[2][MXL_BM * MXL_BK / 16];
+  __shared__ uint4 s_b[2][MXL_BN * MXL_BK / 16];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int h = lane >> 5, li = lane & 31;
+  const int wm = wave >> 1, wn = wave & 1;
+  TileRange tr;
+  if (!schedule_tile<MXL_BM, MXL_BN>(p.t, lane, s_prefix, tr)) return;  // block-uniform
+  const int64_t row_lo = tr.row_lo, row_hi = tr.row_hi, n0 = tr.n0;
+  const uint8_t* bq = p.b_q + (int64_t)tr.g * p.n * p.k;
+  const uint8_t* bsc = p.b_sc + (int64_t)tr.g * p.n * (p.k / 32);
+  const int64_t nblk = p.k / 32;
+
+  // cooperative loader: thread t moves chunks c = t + 256 i (i < 8) of each
+  // operand tile: row c / 8, 16-byte column c % 8 (8 threads per 128-byte row)
+  const int lcol = tid & 7;
+  uint32_t lrow_a[8];
+  uint32_t lmask_a = 0, lmask_b = 0;
 #pragma unroll
-  for (int i = 0; i < VS; ++i)
-#pragma unroll
-    for (int j = 0; j < TN; ++j) acc[i][j] = (f32x16){0};
-  const int64_t nstages = (p.k + MX_BK - 1) / MX_BK;
-  MxStage<TM, TN> r0, r1;
-  if (nstages > 0) mx_load<TM, TN, VS, FAST>(p, p.a_q, p.a_sc, arow, amask, bq, bsc, brow, bmask, h, 0, r0);
-  int64_t s = 0;
-  for (; s + 1 < nstages; s += 2) {
-    mx_load<TM, TN, VS, FAST>(p, p.a_q, p.a_sc, arow, amask, bq, bsc, brow, bmask, h, (s + 1) * MX_BK, r1);
-    mx_compute<TM, TN, VS>(r0, acc);
-    if (s + 2 < nstages) mx_load<TM, TN, VS, FAST>(p, p.a_q, p.a_sc, arow, amask, bq, bsc, brow, bmask, h, (s + 2) * MX_BK, r0);
-    mx_compute<TM, TN, VS>(r1, acc);
+  for (int i = 0; i < 8; ++i) {
+    const int r = (tid >> 3) + 32 * i;
+    const int64_t orow = row_lo + r;
+    int64_t src = -1;
+    if (orow < row_hi) {
+      src = p.row_index ? (int64_t)p.row_index[orow] : orow;
+      if (src < 0 || src >= p.a_rows) src = -1;
+    }
+    lrow_a[i] = src >= 0 ? (uint32_t)src : 0u;
+    lmask_a |= (src >= 0 ? 1u : 0u) << i;
+    lmask_b |= (n0 + r < p.n ? 1u : 0u) << i;
   }
-  if (s < nstages) mx_compute<TM, TN, VS>(r0, acc);
+  // scale rows of this lane's fragments (wave quarter, slab i / j, row li)
+  uint32_t srow_a[4];
+  uint32_t smask_a = 0, smask_b = 0;
 #pragma unroll
-  for (int i = 0; i < VS; ++i) {
+  for (int i = 0; i < 4; ++i) {
+    const int64_t orow = row_lo + 128 * wm + 32 * i + li;
+    int64_t src = -1;
+    if (orow < row_hi) {
+      src = p.row_index ? (int64_t)p.row_index[orow] : orow;
+      if (src < 0 || src >= p.a_rows) src = -1;
+    }
+    srow_a[i] = src >= 0 ? (uint32_t)src : 0u;
+    smask_a |= (src >= 0 ? 1u : 0u) << i;
+    smask_b |= (n0 + 128 * wn + 32 * i + li < p.n ? 1u : 0u) << i;
+  }
+  // B row of loader chunk i / scale slab i (B rows past n use row 0, masked)
+  const int64_t brow0 = n0 + (tid >> 3), bsrow0 = n0 + 128 * wn + li;
+#define NVFP4_MXL_GLOAD(k0, ra, rb, sa, sb)                                                    \
+  do {                                                                                        \
+    const bool kin = FULL || (k0) + 16 * lcol < p.k; /* chunk inside the row (k % 32 == 0) */  \
+    const int64_t ko = kin ? (k0) + 16 * lcol : 0;                                            \
+    _Pragma("unroll") for (int i = 0; i < 8; ++i) {                                           \
+      const bool oka = (lmask_a >> i) & 1u, okb = (lmask_b >> i) & 1u;                        \
+      const uint8_t* pa = (oka ? p.a_q + (int64_t)lrow_a[i] * p.k : p.b_q) + ko;              \
+      const uint8_t* pb = (okb ? bq + (brow0 + 32 * i) * p.k : p.b_q) + ko;                   \
+      ra[i] = *reinterpret_cast<const uint4*>(pa);                                            \
+      rb[i] = *reinterpret_cast<const uint4*>(pb);                                            \
+    }                                                                                         \
+    _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                           \
+      const bool oka = (smask_a >> i) & 1u, okb = (smask_b >> i) & 1u;                        \
+      sa[i] = mx_scales4<FULL>((oka ? p.a_sc + (int64_t)srow_a[i] * nblk : p.b_sc),           \
+                               (k0) / 32, oka ? nblk : 0);                                    \
+      sb[i] = mx_scales4<FULL>((okb ? bsc + (bsrow0 + 32 * i) * nblk : p.b_sc), (k0) / 32,    \
+                               okb ? nblk : 0);                                               \
+    }                                                                                         \
+  } while (0)
+#define NVFP4_MXL_LWRITE(buf, k0, ra, rb)                                              \
+  do {                                                                                \
+    const bool kin = FULL || (k0) + 16 * lcol < p.k;                                  \
+    _Pragma("unroll") for (int i = 0; i < 8; ++i) {                                   \
+      const int r = (tid >> 3) + 32 * i;                                              \
+      const int slot = r * 8 + (lcol ^ mxl_swz(r));                                   \
+      s_a[buf][slot] = keep_if(kin && ((lmask_a >> i) & 1u), ra[i]);                  \
+      s_b[buf][slot] = keep_if(kin && ((lmask_b >> i) & 1u), rb[i]);                  \
+    }                                                                                 \
+  } while (0)
+
+  f32x16 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = (f32x16){0};
+
+  const int64_t nstages = (p.k + MXL_BK - 1) / MXL_BK;
+  uint4 ra[8], rb[8];
+  uint32_t sa_cur[4], sb_cur[4], sa_nxt[4], sb_nxt[4];
+  if (nstages > 0) {
+    NVFP4_MXL_GLOAD(0, ra, rb, sa_cur, sb_cur);
+    NVFP4_MXL_LWRITE(0, 0, ra, rb);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      sa_cur[i] = ((smask_a >> i) & 1u) ? sa_cur[i] : 0x7F7F7F7Fu;
+      sb_cur[i] = ((smask_b >> i) & 1u) ? sb_cur[i] : 0x7F7F7F7Fu;
+    }
+  }
+  __syncthreads();
+  for (int64_t s = 0; s < nstages; ++s) {
+    const int buf = (int)(s & 1);
+    if (s + 1 < nstages) NVFP4_MXL_GLOAD((s + 1) * MXL_BK, ra, rb, sa_nxt, sb_nxt);
+    // keep the compiler from sinking the loads' consumers (the LDS writes)
+    // above the MFMAs or hoisting both K steps' fragment reads together
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      i32x8 fa[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 128 * wm + 32 * i + li;
+        const uint4 lo = s_a[buf][r * 8 + ((4 * ks + h) ^ mxl_swz(r))];
+        const uint4 hi = s_a[buf][r * 8 + ((4 * ks + 2 + h) ^ mxl_swz(r))];
+        fa[i] = mx_operand(lo, hi);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int c = 128 * wn + 32 * j + li;
+        const uint4 blo = s_b[buf][c * 8 + ((4 * ks + h) ^ mxl_swz(c))];
+        const uint4 bhi = s_b[buf][c * 8 + ((4 * ks + 2 + h) ^ mxl_swz(c))];
+        const i32x8 fb = mx_operand(blo, bhi);
+        const int sbj = (int)((sb_cur[j] >> (8 * (2 * ks + h))) & 0xFFu);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+              fa[i], fb, acc[i][j], 0, 0, 0, (int)((sa_cur[i] >> (8 * (2 * ks + h))) & 0xFFu), 0,
+              sbj);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // the stage's MFMAs are issued before the LDS writes below wait for the
+    // next stage's loads (an empty asm consuming the accumulators pins them)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) asm volatile("" : "+a"(acc[i][j])::"memory");
+    if (s + 1 < nstages) {
+      NVFP4_MXL_LWRITE(buf ^ 1, (s + 1) * MXL_BK, ra, rb);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        sa_cur[i] = ((smask_a >> i) & 1u) ? sa_nxt[i] : 0x7F7F7F7Fu;
+        sb_cur[i] = ((smask_b >> i) & 1u) ? sb_nxt[i] : 0x7F7F7F7Fu;
+      }
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
 #pragma unroll
     for (int rr = 0; rr < 16; ++rr) {
-      const int64_t row = row_lo + 32 * i + 8 * (rr >> 2) + 4 * h + (rr & 3);
+      const int64_t row = row_lo + 128 * wm + 32 * i + 8 * (rr >> 2) + 4 * h + (rr & 3);
       if (row >= row_hi) continue;
       float* yr = p.y + row * p.n;
 #pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        const int64_t col = n0 + 32 * j + li;
+      for (int j = 0; j < 4; ++j) {
+        const int64_t col = n0 + 128 * wn + 32 * j + li;
         if (col < p.n) yr[col] = acc[i][j][rr];
       }
     }
   }
-}
-
-template <int TM, int TN, bool FAST>
-__global__ __launch_bounds__(64) void mxfp8_gemm_kernel(MxGemmArgs p) {
-  constexpr int BM = 32 * TM, BN = 32 * TN;
-  __shared__ int32_t s_prefix[MAX_GROUPS + 1];
-  const int lane = threadIdx.x;
-  const int h = lane >> 5, li = lane & 31;
-  TileRange tr;
-  if (!schedule_tile<BM, BN>(p.t, lane, s_prefix, tr)) return;  // block-uniform
-  const int64_t row_lo = tr.row_lo, row_hi = tr.row_hi, n0 = tr.n0;
-  const uint8_t* bq_base = p.b_q + (int64_t)tr.g * p.n * p.k;
-  const uint8_t* bsc_base = p.b_sc + (int64_t)tr.g * p.n * (p.k / 32);
-  uint32_t arow[TM], brow[TN];
-  uint32_t amask = 0, bmask = 0;
-#pragma unroll
-  for (int i = 0; i < TM; ++i) {
-    const int64_t orow = row_lo + 32 * i + li;
-    int64_t r = -1;
-    if (orow < row_hi) {
-      r = p.row_index ? (int64_t)p.row_index[orow] : orow;
-      if (r < 0 || r >= p.a_rows) r = -1;
-    }
-    arow[i] = r >= 0 ? (uint32_t)r : 0u;
-    amask |= (r >= 0 ? 1u : 0u) << i;
-  }
-#pragma unroll
-  for (int j = 0; j < TN; ++j) {
-    const int64_t c = n0 + 32 * j + li;
-    brow[j] = c < p.n ? (uint32_t)c : 0u;
-    bmask |= (c < p.n ? 1u : 0u) << j;
-  }
-  const int vslabs = (int)min((int64_t)TM, (row_hi - row_lo + 31) / 32);
-  static_assert(TM == 4, "slab dispatch is written for TM == 4");
-  switch (vslabs) {
-    case 4: mx_body<TM, TN, 4, FAST>(p, bq_base, bsc_base, arow, amask, brow, bmask, h, li, row_lo, row_hi, n0); break;
-    case 3: mx_body<TM, TN, 3, FAST>(p, bq_base, bsc_base, arow, amask, brow, bmask, h, li, row_lo, row_hi, n0); break;
-    case 2: mx_body<TM, TN, 2, FAST>(p, bq_base, bsc_base, arow, amask, brow, bmask, h, li, row_lo, row_hi, n0); break;
-    default: mx_body<TM, TN, 1, FAST>(p, bq_base, bsc_base, arow, amask, brow, bmask, h, li, row_lo, row_hi, n0); break;
-  }
+#undef NVFP4_MXL_GLOAD
+#undef NVFP4_MXL_LWRITE
 }
 
 static void launch_mx(const MxGemmArgs& a, bool grouped, hipStream_t stream) {
   MxGemmArgs p = a;
-  const int64_t blocks = plan_tiles<128, 128>(p.t, p.n, grouped);
-  const bool fast = (p.k % MX_BK) == 0;  // rows are 16-byte aligned since k % 32 == 0
-  if (fast)
-    hipLaunchKernelGGL((mxfp8_gemm_kernel<4, 4, true>), dim3((unsigned)blocks), dim3(64), 0, stream, p);
+  const int64_t blocks = plan_tiles<MXL_BM, MXL_BN>(p.t, p.n, grouped, 1);
+  if (p.k % MXL_BK == 0)
+    hipLaunchKernelGGL(mxfp8_gemm_lds_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, stream, p);
   else
-    hipLaunchKernelGGL((mxfp8_gemm_kernel<4, 4, false>), dim3((unsigned)blocks), dim3(64), 0, stream, p);
+    hipLaunchKernelGGL(mxfp8_gemm_lds_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, stream,
+                       p);
 }
 
 }  // namespace nvfp4

@@ -17,7 +17,7 @@ struct TileGrid {
   int groups;               // grouped only
   int tiles_n;
   int xcd_n;  // XCD regions along N (8 / xcd_n along M)
-  int slots;  // waves that run at once on one XCD (one per SIMD)
+  int slots;  // blocks that run at once on one XCD
 };
 
 // The block's output tile: rows [row_lo, row_hi) of expert g (0 when dense),
@@ -46,8 +46,8 @@ __device__ __forceinline__ bool schedule_tile(const TileGrid& t, int lane, int32
   if (nlo >= nhi) return false;  // block-uniform
   const int64_t width = nhi - nlo;
   // Region tiles are issued in order; when the last round of a region would
-  // leave more than half of the XCD's wave slots idle, its tiles are issued
-  // as two 64-row halves so that round takes about half as long.
+  // leave more than half of the XCD's slots idle, its tiles are issued as
+  // two halves of BM / 2 rows so that round takes about half as long.
   auto place = [&](int64_t mcount, int64_t& jf, int& hf) -> bool {
     const int64_t T = mcount * width;
     const int64_t tail = T % t.slots;
@@ -124,9 +124,9 @@ __device__ __forceinline__ bool schedule_tile(const TileGrid& t, int lane, int32
     row_lo = mt * BM;
     row_hi = min(t.m_total, row_lo + BM);
   }
-  if (hf >= 0) {  // half tile: rows [row_lo + 64 hf, row_lo + 64 hf + 64)
-    row_lo += 64 * hf;
-    row_hi = min(row_hi, row_lo + 64);
+  if (hf >= 0) {  // half tile: rows [row_lo + (BM/2) hf, row_lo + (BM/2)(hf + 1))
+    row_lo += (BM / 2) * hf;
+    row_hi = min(row_hi, row_lo + BM / 2);
     if (row_lo >= row_hi) return false;  // block-uniform
   }
   out.row_lo = row_lo;
@@ -142,10 +142,11 @@ static inline double split_fill(int64_t tiles, int parts) {
   return per > 0 ? (double)tiles / (double)(per * parts) : 1.0;
 }
 
-// Host launch plan for BM x BN tiles with one wave per SIMD: fills tiles_n,
-// xcd_n and slots and returns the number of one-wave blocks to launch.
+// Host launch plan for BM x BN tiles, `per_cu` blocks resident per CU (4
+// one-wave blocks, or 1 four-wave block): fills tiles_n, xcd_n and slots and
+// returns the number of blocks to launch.
 template <int BM, int BN>
-static int64_t plan_tiles(TileGrid& t, int64_t n, bool grouped) {
+static int64_t plan_tiles(TileGrid& t, int64_t n, bool grouped, int per_cu = 4) {
   t.tiles_n = (int)((n + BN - 1) / BN);
   // upper bound on m-tiles (grouped: each group adds at most a partial tile;
   // the exact count is derived on the device from the offsets)
@@ -160,7 +161,7 @@ static int64_t plan_tiles(TileGrid& t, int64_t n, bool grouped) {
       if (f >= best) { best = f; t.xcd_n = xn; }
     }
   }
-  t.slots = (nvfp4host::num_cus() / 8) * 4;
+  t.slots = (nvfp4host::num_cus() / 8) * per_cu;
   if (t.slots < 2) t.slots = 2;
   const int64_t per_xcd = ((tiles_m + (8 / t.xcd_n) - 1) / (8 / t.xcd_n)) *
                               ((t.tiles_n + t.xcd_n - 1) / t.xcd_n) +
