@@ -28,13 +28,23 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "nvfp4_oracle.c")
 _LIB = os.path.join(_HERE, "libnvfp4_oracle.so")
+# an alternative build of the same source (the mutation tests load builds
+# with one planted mistake each); used as given, never rebuilt here
+_LIB_OVERRIDE = os.environ.get("NVFP4_ORACLE_LIB")
 
 GCC_FLAGS = ["-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp", "-ffp-contract=off",
              "-fno-fast-math", "-fexcess-precision=standard", "-Wall"]
 
 
-def build(force=False):
-    """Compile the oracle with gcc (plain C, IEEE fp32, OpenMP)."""
+def build(force=False, mutant=0, path=None):
+    """Compile the oracle with gcc (plain C, IEEE fp32, OpenMP).  `mutant`
+    plants one of the deliberate mistakes of the mutation tests (0: none);
+    `path` overrides the output file."""
+    if mutant or path:
+        out = path or (_LIB + ".mut%d" % mutant)
+        subprocess.check_call(["gcc"] + GCC_FLAGS + ["-DORACLE_MUTANT=%d" % mutant, _SRC, "-o", out,
+                                                    "-lm"])
+        return out
     if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
         tmp = _LIB + ".tmp%d" % os.getpid()
         subprocess.check_call(["gcc"] + GCC_FLAGS + [_SRC, "-o", tmp, "-lm"])
@@ -48,8 +58,11 @@ _lib = None
 def lib():
     global _lib
     if _lib is None:
-        build()
-        L = ctypes.CDLL(_LIB)
+        if _LIB_OVERRIDE:
+            L = ctypes.CDLL(_LIB_OVERRIDE)
+        else:
+            build()
+            L = ctypes.CDLL(_LIB)
         P = ctypes.c_void_p
         I64 = ctypes.c_int64
         L.oracle_threads.restype = ctypes.c_int

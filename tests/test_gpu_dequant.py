@@ -53,6 +53,17 @@ def test_dequantize_every_scale_and_code():
     check(q, sb, s, what="exhaustive codes")
 
 
+def test_dequantize_fp32_halfway_cases():
+    """Outer scales for which 1.5 * S rounds in fp32 exactly onto a bf16
+    halfway point: the kernel's correction branch decides these."""
+    from test_oracle_dequant import fp32_tie_scales
+    s = fp32_tie_scales(512)
+    rows = len(s)
+    q = np.tile(np.array([0x33, 0xBB, 0x53, 0x3B, 0x35, 0x73, 0xB3, 0x37], np.uint8), (rows, 1))
+    sb = np.full((rows, 1), 0x38, np.uint8)
+    check(q, sb, s, what="fp32 halfway cases")
+
+
 def test_dequantize_tie_heavy_scales():
     q, sb, s = oracle_rows(2, "x")
     s = (s.view(np.uint32) & np.uint32(0xFFFF0000)).view(np.float32).copy()  # 8 significant bits

@@ -120,3 +120,37 @@ def test_dequantize_weight_scale_index(oracle):
     for g in range(3):
         part = oracle.dequantize_bf16(q[g], sb[g], np.repeat(s[g], 40))
         assert np.array_equal(out[40 * g:40 * (g + 1)], part)
+
+
+def fp32_tie_scales(count=64):
+    """Outer scales S (fp32) for which 1.5 * S, rounded to fp32, lands exactly
+    on a bf16 halfway point while the exact product does not: rounding twice
+    (via fp32) and once disagree there."""
+    m = np.arange(1 << 23, 1 << 24, dtype=np.int64)
+    exact = 3 * m                                  # 1.5 * S in units of 2^-24 (S = m * 2^-23)
+    f = (exact.astype(np.float64)).astype(np.float32)
+    bits = f.view(np.uint32)
+    hit = ((bits & 0xFFFF) == 0x8000) & (f.astype(np.float64) != exact.astype(np.float64))
+    ms = m[hit][:count]
+    return (ms.astype(np.float64) * 2.0 ** -23).astype(np.float32)
+
+
+def test_dequantize_single_rounding_at_fp32_ties(oracle):
+    s = fp32_tie_scales(256)
+    double_rounded = oracle.f32_to_bf16((1.5 * s.astype(np.float64)).astype(np.float32))
+    keep = [r for r in range(len(s)) if int(double_rounded[r]) != nearest_bf16_fraction(1.5 * float(s[r]))]
+    s = s[keep][:64]
+    assert len(s) >= 16
+    rows = len(s)
+    q = np.full((rows, 8), 0x33, np.uint8)           # every element code 3: e2m1 = 1.5
+    q[:, 1] = 0xBB                                   # and -1.5
+    sb = np.full((rows, 1), 0x38, np.uint8)          # block scale 1.0
+    out = oracle.dequantize_bf16(q, sb, s)
+    double_rounded = oracle.f32_to_bf16((1.5 * s.astype(np.float64)).astype(np.float32))
+    differs = 0
+    for r in range(rows):
+        want = nearest_bf16_fraction(1.5 * float(s[r]))
+        assert int(out[r, 0]) == want
+        assert int(out[r, 2]) == want | 0x8000 or int(out[r, 3]) == want | 0x8000
+        differs += int(double_rounded[r]) != want
+    assert differs == rows                           # every case separates the two roundings
