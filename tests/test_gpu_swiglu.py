@@ -66,6 +66,25 @@ def test_swiglu_magnitude_ranges(gstd, ustd):
     check_against_oracle(gu, run_all(gu), "gstd=%g ustd=%g" % (gstd, ustd))
 
 
+def test_swiglu_wide_range_and_thresholds():
+    """The kernel evaluates most elements in fp32 and re-evaluates in fp64
+    those whose fp32 result lies near a bf16 rounding boundary, below 2^-100,
+    or whose gate is below -80; exp(-g) is skipped for g >= 20.  Gates span
+    [-90, 30] (across both thresholds, plus a dense grid around each) and up
+    magnitudes 2^-120 .. 2^100, so results cover tiny, denormal and huge
+    values, and some 1 in 2000 fall inside the rounding test's window."""
+    rows, f = 128, 1024
+    n = rows * f
+    g = sg.uniform(11, sg.S_MISC, n) * 120.0 - 90.0
+    g[:4096] = np.linspace(-80.01, -79.99, 4096)
+    g[4096:8192] = np.linspace(19.99, 20.01, 4096)
+    e = np.floor(sg.uniform(12, sg.S_MISC, n) * 220.0) - 120.0
+    u = np.ldexp(sg.uniform(13, sg.S_MISC, n) + 0.5, e.astype(np.int64))
+    u = np.where(sg.uniform(14, sg.S_MISC, n) < 0.5, -u, u)
+    gu = np.concatenate([g.reshape(rows, f), u.reshape(rows, f)], axis=1).astype(np.float32)
+    check_against_oracle(gu, run_all(gu), "wide range")
+
+
 def test_swiglu_zero_and_special_rows():
     rows, f = 6, 256
     gu = gate_up_input(rows, f, seed=5)
