@@ -319,6 +319,16 @@ int nvfp4_debug_encode_e2m1(const float* v, int64_t n, uint8_t* code, void* stre
  * and +-0 are specified (the quantizer never converts larger values). */
 int nvfp4_debug_encode_fp8(const float* v, int64_t n, uint8_t* code, void* stream);
 int nvfp4_debug_encode_e4m3(const float* v, int64_t n, uint8_t* code, void* stream);
+/* nvfp4_debug_block_scale: the quantizer's per-block scale step (Miles page,
+ * section 速读: E4M3 block scale under the FP32 outer scale) on arbitrary
+ * inputs.  For each i, with S = fl32(amax[i] / 2688) and a = the bf16 value
+ * of block_amax[i] (sign bit ignored):
+ *   code[i] = RNE_SAT_E4M3(fl32(a / fl32(6 S)))   (0 when S == 0)
+ *   inv[i]  = fl32(1 / fl32(S * e4m3(code[i])))    (0 when that product is 0)
+ * block_amax [n] u16 (bf16 bits), amax [n] f32, code [n] u8, inv [n] f32,
+ * all device memory.  amax[i] must be finite and >= 0.  Errors as above. */
+int nvfp4_debug_block_scale(const uint16_t* block_amax, const float* amax, int64_t n,
+                            uint8_t* code, float* inv, void* stream);
 
 #ifdef __cplusplus
 }

@@ -63,11 +63,13 @@ def lib():
         L.nvfp4_debug_encode_fp8.argtypes = [P, I64, P, P]
         L.nvfp4_debug_encode_e2m1.argtypes = [P, I64, P, P]
         L.nvfp4_debug_encode_e4m3.argtypes = [P, I64, P, P]
+        L.nvfp4_debug_block_scale.argtypes = [P, P, I64, P, P, P]
         for f in ("nvfp4_quantize_rows", "nvfp4_quantize_weight", "nvfp4_gemm",
                   "nvfp4_swiglu_quantize_rows", "nvfp4_moe_route", "nvfp4_dequantize_rows",
                   "nvfp4_mxfp8_quantize_rows", "nvfp4_debug_encode_fp8", "nvfp4_mxfp8_gemm",
                   "nvfp4_mxfp8_grouped_gemm",
-                  "nvfp4_grouped_gemm", "nvfp4_debug_encode_e2m1", "nvfp4_debug_encode_e4m3"):
+                  "nvfp4_grouped_gemm", "nvfp4_debug_encode_e2m1", "nvfp4_debug_encode_e4m3",
+                  "nvfp4_debug_block_scale"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -368,6 +370,22 @@ def nvfp4_debug_encode_e4m3(v):
     _check("nvfp4_debug_encode_e4m3",
            lib().nvfp4_debug_encode_e4m3(_ptr(v), v.numel(), _ptr(out), _stream(v.device)))
     return out
+
+
+def nvfp4_debug_block_scale(block_amax, amax):
+    """The quantizer's block-scale step on arbitrary inputs: block_amax int16
+    (bf16 bits of a block's largest magnitude) and amax float32 (the row's
+    amax), same shape.  Returns (code uint8, inv float32)."""
+    _dev(block_amax, "block_amax", (torch.int16,))
+    _dev(amax, "amax", (torch.float32,))
+    if block_amax.shape != amax.shape:
+        raise ValueError("block_amax and amax differ in shape")
+    code = torch.empty(amax.shape, dtype=torch.uint8, device=amax.device)
+    inv = torch.empty(amax.shape, dtype=torch.float32, device=amax.device)
+    _check("nvfp4_debug_block_scale",
+           lib().nvfp4_debug_block_scale(_ptr(block_amax), _ptr(amax), amax.numel(), _ptr(code),
+                                         _ptr(inv), _stream(amax.device)))
+    return code, inv
 
 
 def nvfp4_debug_encode_fp8(v):

@@ -55,6 +55,20 @@ __global__ __launch_bounds__(256) void debug_e4m3_kernel(const float* __restrict
   if (i < n) code[i] = (uint8_t)e4m3_encode(v[i]);
 }
 
+__global__ __launch_bounds__(256) void debug_block_scale_kernel(const uint16_t* __restrict__ bmax,
+                                                                const float* __restrict__ amax,
+                                                                int64_t n,
+                                                                uint8_t* __restrict__ code,
+                                                                float* __restrict__ inv) {
+  int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n) return;
+  uint32_t c;
+  float r;
+  block_scale(bmax[i] & 0x7FFFu, row_scale(amax[i]), c, r);
+  code[i] = (uint8_t)c;
+  inv[i] = r;
+}
+
 }  // namespace nvfp4
 
 extern "C" {
@@ -95,6 +109,23 @@ int nvfp4_debug_encode_e2m1(const float* v, int64_t n, uint8_t* code, void* stre
 
 int nvfp4_debug_encode_e4m3(const float* v, int64_t n, uint8_t* code, void* stream) {
   return debug_launch(1, v, n, code, stream);
+}
+
+int nvfp4_debug_block_scale(const uint16_t* block_amax, const float* amax, int64_t n,
+                            uint8_t* code, float* inv, void* stream) {
+  if (n < 0) return NVFP4_ERROR_INVALID_VALUE;
+  if (n == 0) return NVFP4_SUCCESS;
+  if (!block_amax || !amax || !code || !inv) return NVFP4_ERROR_INVALID_VALUE;
+  if (!nvfp4host::aligned(block_amax, 2) || !nvfp4host::aligned(amax, 4) ||
+      !nvfp4host::aligned(inv, 4))
+    return NVFP4_ERROR_MISALIGNED;
+  if (n > ((int64_t)1 << 40)) return NVFP4_ERROR_UNSUPPORTED_SHAPE;
+  int st = nvfp4host::check_arch();
+  if (st) return st;
+  dim3 grid((unsigned)((n + 255) / 256));
+  hipLaunchKernelGGL(nvfp4::debug_block_scale_kernel, grid, dim3(256), 0, (hipStream_t)stream,
+                     block_amax, amax, n, code, inv);
+  return nvfp4host::launch_status();
 }
 
 }  // extern "C"

@@ -41,15 +41,16 @@ __device__ __forceinline__ uint32_t block_amax_bits(const uint4& a, const uint4&
 
 // ------------------------------------------------------------ E4M3 codec --
 // RNE_SAT onto E4M3 (OCP FN, bias 7, max 448) for v >= 0 or +inf.  Values at
-// or above 448 saturate; below 2^-6 the grid is the subnormal step 2^-9 and
-// round-to-nearest-even on v * 2^9 is exact; otherwise the fp32 mantissa is
-// rounded to 3 bits with ties to even (a carry moves into the exponent).
+// or above 448 (and NaN) saturate; below 2^-6 the grid is the subnormal step
+// 2^-9 and round-to-nearest-even on v * 2^9 is exact; otherwise the fp32
+// mantissa is rounded to 3 bits with ties to even (a carry moves into the
+// exponent).  Branch-free: all three candidates are formed and one selected.
 __device__ __forceinline__ uint32_t e4m3_encode(float v) {
-  if (!(v < 448.0f)) return 0x7Eu;
-  if (v < 0.015625f) return (uint32_t)__builtin_rintf(v * 512.0f);
-  uint32_t u = __float_as_uint(v);
-  u += 0x7FFFFu + ((u >> 20) & 1u);
-  return (u >> 20) - (120u << 3);
+  const uint32_t u = __float_as_uint(v);
+  const uint32_t nrm = ((u + 0x7FFFFu + ((u >> 20) & 1u)) >> 20) - (120u << 3);
+  const uint32_t sub = (uint32_t)__builtin_rintf(__builtin_fminf(v, 1.0f) * 512.0f);
+  const uint32_t c = (v < 0.015625f) ? sub : nrm;
+  return (v < 448.0f) ? c : 0x7Eu;
 }
 
 // Exact fp32 value of an E4M3 code 0..0x7E.
@@ -60,14 +61,60 @@ __device__ __forceinline__ float e4m3_decode(uint32_t c) {
   return e ? nrm : sub;
 }
 
+// Per-row (or per-group) scale terms: S = fl32(amax / 2688), t = fl32(6 S)
+// and rt = fl32(1 / t), each correctly rounded.  `fast` says whether the
+// quotients a_b / t of this row may be formed from rt (t well inside the
+// normal range, so no intermediate below overflows or underflows).
+struct RowScale {
+  float S, t, rt;
+  bool fast;
+};
+
+__device__ __forceinline__ RowScale row_scale(float amax) {
+  RowScale r;
+  r.S = amax / 2688.0f;
+  r.t = 6.0f * r.S;
+  r.fast = r.t >= 0x1p-100f && r.t <= 0x1p100f;
+  r.rt = r.fast ? 1.0f / r.t : 0.0f;
+  return r;
+}
+
 // Block scale code and reciprocal of d = S * s_b for one block whose largest
-// magnitude has the bf16 bit pattern amax_bits (t = 6 * S).
-__device__ __forceinline__ void block_scale(uint32_t amax_bits, float S, float t, uint32_t& code,
+// magnitude has the bf16 bit pattern amax_bits:
+//   code = RNE_SAT_E4M3(fl32(a_b / t)),  inv = fl32(1 / fl32(S * s_b)).
+// Both fp32 results are the correctly rounded ones, formed with fma
+// corrections instead of full divisions:
+//  - quotient: q = fl32(a * rt), r = a - q t (exact in an fma), v = fl32(q +
+//    r rt).  With rt the correctly rounded 1/t this is the correctly rounded
+//    a / t for every bf16 significand of a and every fp32 significand of t
+//    (an exhaustive check over all 2^30 pairs; exponents only scale the
+//    values while nothing under- or overflows).  A subnormal a gives a
+//    quotient far below 2^-10, where the code is 0 either way; a quotient
+//    that overflows gives NaN or inf, which saturates like the exact one.
+//  - reciprocal: y0 = v_rcp_f32(d) (within 1 ulp), e = 1 - d y0 (exact in an
+//    fma), inv = fl32(y0 + e y0): correctly rounded for every fp32
+//    significand and every y0 within 1 ulp of 1/d except the significand of
+//    all ones (an exhaustive check), which takes the full division, as do
+//    d outside [2^-125, 2^121) and d = 0 (inv = 0 there).
+__device__ __forceinline__ void block_scale(uint32_t amax_bits, const RowScale& rs, uint32_t& code,
                                             float& inv) {
-  float ab = __uint_as_float(amax_bits << 16);
-  code = (S == 0.0f) ? 0u : e4m3_encode(ab / t);
-  float d = S * e4m3_decode(code);
-  inv = (d != 0.0f) ? 1.0f / d : 0.0f;
+  const float ab = __uint_as_float(amax_bits << 16);
+  float v;
+  if (rs.fast) {
+    const float q = ab * rs.rt;
+    v = __builtin_fmaf(__builtin_fmaf(-q, rs.t, ab), rs.rt, q);
+  } else {
+    v = ab / rs.t;
+  }
+  code = (rs.S == 0.0f) ? 0u : e4m3_encode(v);
+  const float d = rs.S * e4m3_decode(code);
+  const uint32_t db = __float_as_uint(d);
+  if (__builtin_expect(db - 0x01000000u < 0x7C000000u - 0x01000000u && (db & 0x7FFFFFu) != 0x7FFFFFu, 1)) {
+    const float y0 = __builtin_amdgcn_rcpf(d);
+    inv = __builtin_fmaf(__builtin_fmaf(-d, y0, 1.0f), y0, y0);
+  } else {
+    inv = (d != 0.0f) ? 1.0f / d : 0.0f;
+  }
 }
 
 // ------------------------------------------------------------ E2M1 codec --

@@ -10,16 +10,18 @@
 //
 // Kernel layout (HBM-bound: 2.5625 bytes move per element):
 //  - L lanes of a wave64 own one row (L = 16, 32 or 64 chosen so the row's
-//    16-element blocks divide evenly); lane j owns blocks j, j+L, j+2L, ...
-//    and keeps them in VGPRs, so the row is read from HBM once.
-//  - Each block is 32 contiguous bytes (two 16-byte loads); consecutive
-//    lanes read consecutive blocks, so a wave's loads are contiguous.
-//  - Block amax: packed 16-bit max over the bf16 magnitude bits (exact:
-//    non-negative bf16 bit patterns order like their values).
+//    16-byte half-blocks divide evenly); lane j owns half-blocks j, j+L,
+//    j+2L, ... (8 elements each) and keeps them in VGPRs, so the row is read
+//    from HBM once.  Every load instruction reads L * 16 contiguous bytes.
+//  - A block's two halves sit in lanes 2m and 2m+1: each lane takes the
+//    packed 16-bit max over its 8 bf16 magnitude bits (exact: non-negative
+//    bf16 bit patterns order like their values) and one DPP swap combines
+//    the pair, so both lanes hold the block amax and derive the same scale.
 //  - Row amax: DPP / ds_swizzle / readlane max over the row's lanes.
 //  - Per block one correctly rounded division (a_b / 6S) and one correctly
 //    rounded reciprocal (1 / d); per element one fp32 multiply and half of a
-//    gfx950 pack-convert to E2M1 (two elements per instruction).
+//    gfx950 pack-convert to E2M1 (two elements per instruction).  Each lane
+//    stores one dword of codes per half-block; even lanes store the scale.
 #include "nvfp4_internal.h"
 
 namespace nvfp4 {
@@ -33,112 +35,123 @@ enum QuantMode { MODE_ROW = 0, MODE_AMAX_IN = 1, MODE_GROUP = 2 };
 __device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
-// Encode one block of 16 elements (two uint4 of bf16) with reciprocal `inv`
-// into 8 bytes of E2M1 codes.  When inv is +inf (d is a tiny denormal) x * inv
-// would be NaN for x = +-0, so zeros are passed through unchanged there.
-__device__ __forceinline__ uint2 encode_block(const uint4& a, const uint4& b, float inv) {
-  uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-  float r[16];
+// Encode one half-block of 8 elements (a uint4 of bf16) with reciprocal
+// `inv` into a dword of E2M1 codes.  When inv is +inf (d is a tiny denormal)
+// x * inv would be NaN for x = +-0, so zeros are passed through unchanged.
+__device__ __forceinline__ uint32_t encode_half(const uint4& a, float inv) {
+  const uint32_t w[4] = {a.x, a.y, a.z, a.w};
+  float r[8];
   if (__builtin_expect(__builtin_isinf(inv), 0)) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < 4; ++i) {
       float lo = bf16lo(w[i]), hi = bf16hi(w[i]);
       r[2 * i] = (lo == 0.0f) ? lo : lo * inv;
       r[2 * i + 1] = (hi == 0.0f) ? hi : hi * inv;
     }
   } else {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < 4; ++i) {
       r[2 * i] = bf16lo(w[i]) * inv;
       r[2 * i + 1] = bf16hi(w[i]) * inv;
     }
   }
-  uint32_t q0 = 0, q1 = 0;
-  q0 = e2m1_encode2<0>(q0, r[0], r[1]);
-  q0 = e2m1_encode2<1>(q0, r[2], r[3]);
-  q0 = e2m1_encode2<2>(q0, r[4], r[5]);
-  q0 = e2m1_encode2<3>(q0, r[6], r[7]);
-  q1 = e2m1_encode2<0>(q1, r[8], r[9]);
-  q1 = e2m1_encode2<1>(q1, r[10], r[11]);
-  q1 = e2m1_encode2<2>(q1, r[12], r[13]);
-  q1 = e2m1_encode2<3>(q1, r[14], r[15]);
-  return make_uint2(q0, q1);
+  uint32_t q = 0;
+  q = e2m1_encode2<0>(q, r[0], r[1]);
+  q = e2m1_encode2<1>(q, r[2], r[3]);
+  q = e2m1_encode2<2>(q, r[4], r[5]);
+  q = e2m1_encode2<3>(q, r[6], r[7]);
+  return q;
 }
 
-// The NB blocks of one row group held by a lane (one 32-byte block is two
-// uint4 of bf16).
-template <int NB>
+// Max of the 8 bf16 magnitudes in a uint4 (as a bf16 bit pattern).
+__device__ __forceinline__ uint32_t half_amax_bits(const uint4& a) {
+  const uint32_t M = 0x7FFF7FFFu;
+  const u16x2 m = __builtin_elementwise_max(
+      __builtin_elementwise_max(__builtin_bit_cast(u16x2, a.x & M), __builtin_bit_cast(u16x2, a.y & M)),
+      __builtin_elementwise_max(__builtin_bit_cast(u16x2, a.z & M), __builtin_bit_cast(u16x2, a.w & M)));
+  return max((uint32_t)m.x, (uint32_t)m.y);
+}
+
+// The U half-blocks of one row group held by a lane, and the row's supplied
+// amax (row or group) when there is one.  The amax load is issued before the
+// row's data loads: vector memory counters retire in order, so waiting for
+// the data then also covers the amax, and nothing forces a wait on a load
+// issued later (the next group's prefetch).
+template <int U>
 struct RowData {
-  uint4 d[NB][2];
+  uint4 d[U];
+  float amax;
+  int64_t gi;  // group of the row (MODE_GROUP)
 };
 
-template <int L, int NB>
+template <int L, int U, int MODE>
 __device__ __forceinline__ void load_rows(const uint16_t* __restrict__ x, int64_t rows, int64_t k,
-                                          int nblk, int64_t row, int j, RowData<NB>& r) {
+                                          int nh, int64_t row, int j,
+                                          const float* __restrict__ amax_src,
+                                          int64_t rows_per_group, RowData<U>& r) {
   const bool row_ok = row < rows;
+  if (MODE == MODE_AMAX_IN) {
+    r.amax = row_ok ? amax_src[row] : 0.0f;
+  } else if (MODE == MODE_GROUP) {
+    r.gi = row_ok ? row / rows_per_group : 0;
+    r.amax = row_ok ? amax_src[r.gi] : 0.0f;
+  }
   const uint4* xr = reinterpret_cast<const uint4*>(x + (row_ok ? row : 0) * k);
 #pragma unroll
-  for (int i = 0; i < NB; ++i) {
-    const int b = j + L * i;
-    if (row_ok && b < nblk) {
-      r.d[i][0] = ld_stream(xr + 2 * b);
-      r.d[i][1] = ld_stream(xr + 2 * b + 1);
-    } else {
-      r.d[i][0] = make_uint4(0, 0, 0, 0);
-      r.d[i][1] = make_uint4(0, 0, 0, 0);
-    }
+  for (int i = 0; i < U; ++i) {
+    const int h = j + L * i;
+    r.d[i] = (row_ok && h < nh) ? ld_stream(xr + h) : make_uint4(0, 0, 0, 0);
   }
 }
 
+// Block amax of the half-block held by this lane and its partner (lane ^ 1).
+__device__ __forceinline__ uint32_t pair_max(uint32_t v) {
+  return max(v, dpp_mov<0xB1>(v));  // quad_perm [1,0,3,2]
+}
+
 // Encode and store one row group.  Must be called by all 64 lanes of the
-// wave (the row amax is a cross-lane reduction).
-template <int L, int NB, int MODE>
-__device__ __forceinline__ void encode_rows(const RowData<NB>& r, int64_t rows, int64_t k,
-                                            int nblk, int64_t row, int j,
+// wave (block and row amax are cross-lane reductions).
+template <int L, int U, int MODE>
+__device__ __forceinline__ void encode_rows(const RowData<U>& r, int64_t rows, int64_t k, int nh,
+                                            int64_t row, int j,
                                             const float* __restrict__ amax_src,
                                             int64_t rows_per_group, uint8_t* __restrict__ q,
                                             uint8_t* __restrict__ sb, float* __restrict__ s) {
   const bool row_ok = row < rows;
-  uint32_t bmax[NB];
+  uint32_t bmax[U];
   uint32_t rmax = 0;
 #pragma unroll
-  for (int i = 0; i < NB; ++i) {
-    bmax[i] = block_amax_bits(r.d[i][0], r.d[i][1]);
+  for (int i = 0; i < U; ++i) {
+    bmax[i] = pair_max(half_amax_bits(r.d[i]));
     rmax = max(rmax, bmax[i]);
   }
-  float amax;
-  if (MODE == MODE_ROW) {
-    amax = __uint_as_float(group_max_u32<L>(rmax) << 16);
-  } else if (MODE == MODE_AMAX_IN) {
-    amax = row_ok ? amax_src[row] : 0.0f;
-  } else {
-    amax = row_ok ? amax_src[row / rows_per_group] : 0.0f;
-  }
-  const float S = amax / 2688.0f;
-  if (MODE != MODE_GROUP && row_ok && j == 0) s[row] = S;
-  const float t = 6.0f * S;
-  uint8_t* qr = q + (row_ok ? row : 0) * (k / 2);
+  const float amax = (MODE == MODE_ROW) ? __uint_as_float(group_max_u32<L>(rmax) << 16) : r.amax;
+  const RowScale rs = row_scale(amax);
+  if (MODE != MODE_GROUP && row_ok && j == 0) s[row] = rs.S;
+  // the group's first row also stores its outer scale (when asked to)
+  if (MODE == MODE_GROUP && s && row_ok && j == 0 && row == r.gi * rows_per_group) s[r.gi] = rs.S;
+  uint32_t* qr = reinterpret_cast<uint32_t*>(q + (row_ok ? row : 0) * (k / 2));
   uint8_t* sr = sb + (row_ok ? row : 0) * (k / 16);
 #pragma unroll
-  for (int i = 0; i < NB; ++i) {
-    const int b = j + L * i;
-    if (row_ok && b < nblk) {
+  for (int i = 0; i < U; ++i) {
+    const int h = j + L * i;
+    if (row_ok && h < nh) {
       uint32_t code;
       float inv;
-      block_scale(bmax[i], S, t, code, inv);
-      reinterpret_cast<uint2*>(qr)[b] = encode_block(r.d[i][0], r.d[i][1], inv);
-      sr[b] = (uint8_t)code;
+      block_scale(bmax[i], rs, code, inv);
+      qr[h] = encode_half(r.d[i], inv);
+      if ((j & 1) == 0) sr[h >> 1] = (uint8_t)code;
     }
   }
 }
 
-// One row per L lanes (NB blocks per lane at most, nblk <= L * NB); a wave
+// One row per L lanes (U half-blocks per lane at most, nh <= L * U); a wave
 // handles 64 / L rows per row group and walks row groups with a grid stride,
 // loading group i + 1 while it encodes group i (two register buffers,
 // unrolled by two so the buffers never move).
-template <int L, int NB, int MODE>
+template <int L, int U, int MODE>
 __global__ __launch_bounds__(256) void quantize_rows_kernel(
-    const uint16_t* __restrict__ x, int64_t rows, int64_t k, int nblk,
+    const uint16_t* __restrict__ x, int64_t rows, int64_t k, int nh,
     const float* __restrict__ amax_src, int64_t rows_per_group, uint8_t* __restrict__ q,
     uint8_t* __restrict__ sb, float* __restrict__ s) {
   constexpr int RPW = 64 / L;
@@ -148,25 +161,28 @@ __global__ __launch_bounds__(256) void quantize_rows_kernel(
   const int64_t ngroups = (rows + RPW - 1) / RPW;
   const int64_t stride = (int64_t)gridDim.x * 4;
   int64_t g0 = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);  // wave-uniform
-  RowData<NB> r0, r1;
-  if (g0 < ngroups) load_rows<L, NB>(x, rows, k, nblk, g0 * RPW + sub, j, r0);
+  RowData<U> r0, r1;
+  if (g0 < ngroups)
+    load_rows<L, U, MODE>(x, rows, k, nh, g0 * RPW + sub, j, amax_src, rows_per_group, r0);
   for (; g0 < ngroups; g0 += 2 * stride) {
     const int64_t g1 = g0 + stride, g2 = g1 + stride;
-    if (g1 < ngroups) load_rows<L, NB>(x, rows, k, nblk, g1 * RPW + sub, j, r1);
-    encode_rows<L, NB, MODE>(r0, rows, k, nblk, g0 * RPW + sub, j, amax_src, rows_per_group, q,
-                             sb, s);
-    if (g2 < ngroups) load_rows<L, NB>(x, rows, k, nblk, g2 * RPW + sub, j, r0);
     if (g1 < ngroups)
-      encode_rows<L, NB, MODE>(r1, rows, k, nblk, g1 * RPW + sub, j, amax_src, rows_per_group,
-                               q, sb, s);
+      load_rows<L, U, MODE>(x, rows, k, nh, g1 * RPW + sub, j, amax_src, rows_per_group, r1);
+    encode_rows<L, U, MODE>(r0, rows, k, nh, g0 * RPW + sub, j, amax_src, rows_per_group, q, sb,
+                            s);
+    if (g2 < ngroups)
+      load_rows<L, U, MODE>(x, rows, k, nh, g2 * RPW + sub, j, amax_src, rows_per_group, r0);
+    if (g1 < ngroups)
+      encode_rows<L, U, MODE>(r1, rows, k, nh, g1 * RPW + sub, j, amax_src, rows_per_group, q,
+                              sb, s);
   }
 }
 
-// Rows longer than 64 * 8 blocks: one wave per row, two passes (the second
-// re-reads the row, mostly from L2).
+// Rows longer than 64 * 16 half-blocks: one wave per row, two passes (the
+// second re-reads the row, mostly from L2).
 template <int MODE>
 __global__ __launch_bounds__(256) void quantize_rows_long_kernel(
-    const uint16_t* __restrict__ x, int64_t rows, int64_t k, int nblk,
+    const uint16_t* __restrict__ x, int64_t rows, int64_t k, int nh,
     const float* __restrict__ amax_src, int64_t rows_per_group, uint8_t* __restrict__ q,
     uint8_t* __restrict__ sb, float* __restrict__ s) {
   const int lane = threadIdx.x & 63;
@@ -176,25 +192,31 @@ __global__ __launch_bounds__(256) void quantize_rows_long_kernel(
   float amax;
   if (MODE == MODE_ROW) {
     uint32_t rmax = 0;
-    for (int b = lane; b < nblk; b += 64) rmax = max(rmax, block_amax_bits(xr[2 * b], xr[2 * b + 1]));
+    for (int h = lane; h < nh; h += 64) rmax = max(rmax, half_amax_bits(xr[h]));
     amax = __uint_as_float(group_max_u32<64>(rmax) << 16);
   } else if (MODE == MODE_AMAX_IN) {
     amax = amax_src[row];
   } else {
-    amax = amax_src[row / rows_per_group];
+    const int64_t gi = row / rows_per_group;
+    amax = amax_src[gi];
+    if (s && lane == 0 && row == gi * rows_per_group) s[gi] = amax / 2688.0f;
   }
-  const float S = amax / 2688.0f;
-  if (MODE != MODE_GROUP && lane == 0) s[row] = S;
-  const float t = 6.0f * S;
-  uint8_t* qr = q + row * (k / 2);
+  const RowScale rs = row_scale(amax);
+  if (MODE != MODE_GROUP && lane == 0) s[row] = rs.S;
+  uint32_t* qr = reinterpret_cast<uint32_t*>(q + row * (k / 2));
   uint8_t* sr = sb + row * (k / 16);
-  for (int b = lane; b < nblk; b += 64) {
-    uint4 a0 = xr[2 * b], a1 = xr[2 * b + 1];
+  // nh is even and the stride is even, so lanes 2m and 2m+1 stay together
+  // and every lane runs the same number of iterations (DPP needs both).
+  for (int h0 = 0; h0 < nh; h0 += 64) {
+    const int h = h0 + lane;
+    const uint4 a = (h < nh) ? xr[h] : make_uint4(0, 0, 0, 0);
     uint32_t code;
     float inv;
-    block_scale(block_amax_bits(a0, a1), S, t, code, inv);
-    reinterpret_cast<uint2*>(qr)[b] = encode_block(a0, a1, inv);
-    sr[b] = (uint8_t)code;
+    block_scale(pair_max(half_amax_bits(a)), rs, code, inv);
+    if (h < nh) {
+      qr[h] = encode_half(a, inv);
+      if ((lane & 1) == 0) sr[h >> 1] = (uint8_t)code;
+    }
   }
 }
 
@@ -261,9 +283,9 @@ typedef void (*RowKernel)(const uint16_t*, int64_t, int64_t, int, const float*, 
                           uint8_t*, float*);
 
 template <int MODE>
-static RowKernel pick_row_kernel(int nblk, int& lanes) {
+static RowKernel pick_row_kernel(int nh, int& lanes) {
 #define NVFP4_PICK(L)                                                            \
-  switch ((nblk + L - 1) / L) {                                                  \
+  switch ((nh + L - 1) / L) {                                                    \
     case 1: lanes = L; return quantize_rows_kernel<L, 1, MODE>;                  \
     case 2: lanes = L; return quantize_rows_kernel<L, 2, MODE>;                  \
     case 3: lanes = L; return quantize_rows_kernel<L, 3, MODE>;                  \
@@ -272,15 +294,23 @@ static RowKernel pick_row_kernel(int nblk, int& lanes) {
     case 6: lanes = L; return quantize_rows_kernel<L, 6, MODE>;                  \
     case 7:                                                                      \
     case 8: lanes = L; return quantize_rows_kernel<L, 8, MODE>;                  \
+    case 9:                                                                      \
+    case 10: lanes = L; return quantize_rows_kernel<L, 10, MODE>;                \
+    case 11:                                                                     \
+    case 12: lanes = L; return quantize_rows_kernel<L, 12, MODE>;                \
+    case 13:                                                                     \
+    case 14:                                                                     \
+    case 15:                                                                     \
+    case 16: lanes = L; return quantize_rows_kernel<L, 16, MODE>;                \
     default: break;                                                              \
   }
-  // prefer the widest group that divides the row's blocks evenly
-  if (nblk % 64 == 0 && nblk / 64 <= 8) { NVFP4_PICK(64) }
-  if (nblk % 32 == 0 && nblk / 32 <= 8) { NVFP4_PICK(32) }
-  if (nblk % 16 == 0 && nblk / 16 <= 8) { NVFP4_PICK(16) }
-  if (nblk <= 16 * 8 && nblk < 32) { NVFP4_PICK(16) }
-  if (nblk <= 32 * 8 && nblk < 64) { NVFP4_PICK(32) }
-  if (nblk <= 64 * 8) { NVFP4_PICK(64) }
+  // prefer the widest group that divides the row's half-blocks evenly
+  if (nh % 64 == 0 && nh / 64 <= 16) { NVFP4_PICK(64) }
+  if (nh % 32 == 0 && nh / 32 <= 16) { NVFP4_PICK(32) }
+  if (nh % 16 == 0 && nh / 16 <= 16) { NVFP4_PICK(16) }
+  if (nh <= 16 * 16 && nh < 32) { NVFP4_PICK(16) }
+  if (nh <= 32 * 16 && nh < 64) { NVFP4_PICK(32) }
+  if (nh <= 64 * 16) { NVFP4_PICK(64) }
 #undef NVFP4_PICK
   lanes = 0;
   return nullptr;
@@ -290,9 +320,9 @@ template <int MODE>
 static void launch_rows(const uint16_t* x, int64_t rows, int64_t k, const float* amax_src,
                         int64_t rows_per_group, uint8_t* q, uint8_t* sb, float* s,
                         hipStream_t stream) {
-  const int nblk = (int)(k / 16);
+  const int nh = (int)(k / 8);  // 16-byte half-blocks per row
   int lanes = 0;
-  RowKernel kern = pick_row_kernel<MODE>(nblk, lanes);
+  RowKernel kern = pick_row_kernel<MODE>(nh, lanes);
   if (kern) {
     // enough resident waves to keep HBM busy, and several row groups per wave
     // so loads overlap encoding (NVFP4_Q_WAVES_PER_SIMD waves per SIMD)
@@ -300,12 +330,12 @@ static void launch_rows(const uint16_t* x, int64_t rows, int64_t k, const float*
     const int64_t need = (rows + rows_per_block - 1) / rows_per_block;
     const int64_t cap = (int64_t)nvfp4host::num_cus() * NVFP4_Q_WAVES_PER_SIMD;
     dim3 grid((unsigned)(need < cap ? need : cap));
-    hipLaunchKernelGGL(kern, grid, dim3(256), 0, stream, x, rows, k, nblk, amax_src,
+    hipLaunchKernelGGL(kern, grid, dim3(256), 0, stream, x, rows, k, nh, amax_src,
                        rows_per_group, q, sb, s);
   } else {
     dim3 grid((unsigned)((rows + 3) / 4));
     hipLaunchKernelGGL(quantize_rows_long_kernel<MODE>, grid, dim3(256), 0, stream, x, rows, k,
-                       nblk, amax_src, rows_per_group, q, sb, s);
+                       nh, amax_src, rows_per_group, q, sb, s);
   }
 }
 
@@ -377,10 +407,15 @@ extern "C" int nvfp4_quantize_weight(const uint16_t* w_bf16, int64_t groups, int
                          str, w_bf16, group_elems, chunk_vecs, (int)chunks, amax_out);
     }
   }
-  hipLaunchKernelGGL(nvfp4::group_scale_kernel, dim3(gsm), dim3(256), 0, str, groups, amax_in,
-                     amax_out, s);
-  if (rows > 0 && k > 0)
+  // the encode pass stores S[g] itself, except when it does not run or the
+  // amax was supplied (then amax_out also receives a copy of amax_in)
+  const bool enc = rows > 0 && k > 0;
+  const bool s_in_enc = enc && !amax_in;
+  if (!s_in_enc)
+    hipLaunchKernelGGL(nvfp4::group_scale_kernel, dim3(gsm), dim3(256), 0, str, groups, amax_in,
+                       amax_out, s);
+  if (enc)
     nvfp4::launch_rows<nvfp4::MODE_GROUP>(w_bf16, rows, k, amax_in ? amax_in : amax_out,
-                                          rows_per_group, q, sb, s, str);
+                                          rows_per_group, q, sb, s_in_enc ? s : nullptr, str);
   return nvfp4host::launch_status();
 }

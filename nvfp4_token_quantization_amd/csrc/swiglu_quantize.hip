@@ -145,12 +145,11 @@ __global__ __launch_bounds__(256) void swiglu_quantize_kernel(
     }
     if (!row_ok) continue;
     const float amax = __uint_as_float(m << 16);
-    const float S = amax / 2688.0f;
+    const RowScale rs = row_scale(amax);
     if (lw == 0) {
       if (amax_out) amax_out[row] = amax;
-      if (quantize) s[row] = S;
+      if (quantize) s[row] = rs.S;
     }
-    const float t6 = 6.0f * S;
 #pragma unroll
     for (int t = 0; t < T; ++t) {
       const int64_t e0 = 4 * (int64_t)(lw + LANES * t);
@@ -159,7 +158,7 @@ __global__ __launch_bounds__(256) void swiglu_quantize_kernel(
       if (!quantize) continue;
       uint32_t code;
       float inv;
-      block_scale(bmax[t], S, t6, code, inv);
+      block_scale(bmax[t], rs, code, inv);
       float r[4] = {__uint_as_float(hb[t][0] << 16), __uint_as_float(hb[t][0] & 0xFFFF0000u),
                     __uint_as_float(hb[t][1] << 16), __uint_as_float(hb[t][1] & 0xFFFF0000u)};
       if (__builtin_expect(__builtin_isinf(inv), 0)) {

@@ -208,6 +208,11 @@ def test_quantize_weight_groups_and_amax_in():
     fused = np.concatenate([gate, up], axis=1)
     got = nv.nvfp4_quantize_weight(to_dev(fused))
     assert_same_quant(got, oracle.quantize_weight(fused), "fused gate/up")
+    # rows longer than 1024 half-blocks take the one-wave-per-row kernel,
+    # which also stores each group's outer scale
+    wl = sg.normal_bf16(57, 2, (3, 5, 8208), 0.0, 0.02)
+    wl[1, 2, 8000:8016] = 0x7F7F
+    assert_same_quant(nv.nvfp4_quantize_weight(to_dev(wl)), oracle.quantize_weight(wl), "long rows")
     # one group of one row equals per-token quantization of the row
     got1 = nv.nvfp4_quantize_weight(to_dev(w[:1, :1]))
     gotr = nv.nvfp4_quantize_rows(to_dev(w[0, :1]))
@@ -274,3 +279,90 @@ def test_e4m3_codec_exhaustive():
     v = np.array(pts, np.float32)
     got = to_np(nv.nvfp4_debug_encode_e4m3(to_dev(v)))
     assert np.array_equal(got, oracle.rne_sat_e4m3(v))
+
+
+# ------------------------------------------------------------ block scale --
+def _bf16_bits(v):
+    """float32 -> bf16 bit patterns, round to nearest even (finite inputs)."""
+    u = np.ascontiguousarray(v, np.float32).view(np.uint32).astype(np.uint64)
+    return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+
+
+def _block_scale_expected(bbits, amax):
+    """Steps Q2-Q4 of the quantizer in IEEE fp32 (numpy) with the oracle's
+    E4M3 codec: S = amax / 2688, t = 6 S, code = RNE_SAT(a / t) (0 when S is
+    0), inv = 1 / (S * e4m3(code)) (0 when that product is 0)."""
+    S = amax / np.float32(2688.0)
+    t = np.float32(6.0) * S
+    a = (bbits.astype(np.uint32) << 16).view(np.float32)
+    with np.errstate(divide="ignore", invalid="ignore", over="ignore"):
+        v = a / t
+        v = np.where(S == 0, np.float32(0.0), v).astype(np.float32)
+        code = oracle.rne_sat_e4m3(v)
+        d = S * oracle.e4m3_table()[code].astype(np.float32)
+        inv = np.where(d == 0, np.float32(0.0), np.float32(1.0) / d).astype(np.float32)
+    return code, inv
+
+
+def _check_block_scale(bbits, amax, what):
+    code, inv = nv.nvfp4_debug_block_scale(to_dev(bbits.view(np.int16)), to_dev(amax))
+    code, inv = to_np(code), to_np(inv)
+    want_code, want_inv = _block_scale_expected(bbits, amax)
+    bad = np.flatnonzero((code != want_code) | (inv.view(np.uint32) != want_inv.view(np.uint32)))
+    if bad.size:
+        i = bad[0]
+        raise AssertionError("%s: %d mismatches; first a=%#06x amax=%r: code %#x/%#x inv %r/%r" % (
+            what, bad.size, bbits[i], amax[i], code[i], want_code[i], inv[i], want_inv[i]))
+
+
+def test_block_scale_reciprocal_sweep():
+    """The block scale's reciprocal 1 / (S * s_b) over 99% of all fp32
+    significands of the product: every row amax of one binade, with a block
+    amax chosen so the block scale is 1, 1.125, 1.25 or 1.375."""
+    amax = (np.arange(1 << 23, dtype=np.uint32) | np.uint32(127 << 23)).view(np.float32)
+    S = amax / np.float32(2688.0)
+    for m in (1.0, 1.125, 1.25, 1.375):
+        bbits = _bf16_bits(np.float32(m) * (np.float32(6.0) * S))
+        _check_block_scale(bbits, amax, "s_b = %g" % m)
+
+
+def test_block_scale_quotients_and_edges():
+    """Block amax over the full bf16 range against row amaxes spread over
+    fp32's range (so a_b / 6S covers every code, saturation and underflow),
+    plus edge rows: S = 0, subnormal and huge amax (the exact-division
+    fallbacks), block amax above the row amax (amax reuse with a smaller
+    amax_in), subnormal and largest bf16 blocks, and products S * s_b with a
+    significand of all ones."""
+    n = 1 << 22
+    e = np.floor(sg.uniform(91, sg.S_MISC, n) * 250.0) - 125.0
+    amax = np.ldexp(sg.uniform(92, sg.S_MISC, n) + 1.0, e.astype(np.int64)).astype(np.float32)
+    ratio = sg.uniform(93, sg.S_MISC, n) * 1.1
+    ratio = np.where(sg.uniform(94, sg.S_MISC, n) < 0.1, ratio * 1e-3, ratio)
+    bbits = _bf16_bits((amax * ratio).astype(np.float32))
+    _check_block_scale(bbits, amax, "random")
+
+    edges_b, edges_a = [], []
+    specials = [0.0, 1e-45, 1e-40, 1.2e-38, 1e-30, 1e-28, 1.0, 2688.0, 1e28, 1e30, 3e38,
+                np.finfo(np.float32).max]
+    blocks = [0x0000, 0x0001, 0x007F, 0x0080, 0x3F80, 0x43E0, 0x7F7F, 0x7F00, 0x0400]
+    for a in specials:
+        for b in blocks:
+            edges_a.append(a)
+            edges_b.append(b)
+    # S * s_b with an all-ones significand (the reciprocal's fallback): found
+    # among row amaxes in [1, 1.25) for s_b = 1.125 and 1.25, then scaled by
+    # powers of two (which keep the significand)
+    win = (np.arange(1 << 21, dtype=np.uint32) | np.uint32(127 << 23)).view(np.float32)
+    Sw = win / np.float32(2688.0)
+    found = 0
+    for m in (1.125, 1.25):
+        d = Sw * np.float32(m)
+        for i in np.flatnonzero((d.view(np.uint32) & 0x7FFFFF) == 0x7FFFFF):
+            for k in (-60, -20, 0, 20, 60):
+                am = np.float32(np.ldexp(np.float64(win[i]), k))
+                edges_a.append(am)
+                Sk = am / np.float32(2688.0)
+                edges_b.append(int(_bf16_bits(np.array([np.float32(m) * (np.float32(6.0) * Sk)]))[0]))
+                found += 1
+    assert found >= 10
+    _check_block_scale(np.array(edges_b, np.uint16), np.array(edges_a, np.float32), "edges")
