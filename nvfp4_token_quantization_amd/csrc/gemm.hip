@@ -200,7 +200,8 @@ __device__ __forceinline__ void rd_kloop(const GemmArgs& p, const uint8_t* const
   if (s < nstages) rd_compute<TM, TN, VS>(r0, acc);
 }
 
-// Accumulate the tile over K with VS valid A slabs, then scale and store.
+// Accumulate the tile over K with VS valid A slabs, then scale and store
+// (streaming stores: Y is written once and not read back by this kernel).
 template <int TM, int TN, int VS, bool FAST>
 __device__ __forceinline__ void rd_body(const GemmArgs& p, const uint8_t* const* arow,
                                         const uint8_t* const* asrow, const uint8_t* const* brow,
@@ -225,7 +226,7 @@ __device__ __forceinline__ void rd_body(const GemmArgs& p, const uint8_t* const*
 #pragma unroll
       for (int j = 0; j < TN; ++j) {
         const int64_t col = n0 + 32 * j + li;
-        if (col < p.n) yr[col] = acc[i][j][r] * sc;
+        if (col < p.n) __builtin_nontemporal_store(acc[i][j][r] * sc, yr + col);
       }
     }
   }

@@ -220,7 +220,7 @@ __global__ __launch_bounds__(256) void mxfp8_gemm_lds_kernel(MxGemmArgs p) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int64_t col = n0 + 128 * wn + 32 * j + li;
-        if (col < p.n) yr[col] = acc[i][j][rr];
+        if (col < p.n) __builtin_nontemporal_store(acc[i][j][rr], yr + col);
       }
     }
   }
