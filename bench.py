@@ -93,8 +93,8 @@ def gemm_bytes(a_rows, m_out, n, k, groups):
 
 # Launch order of one step and the number of kernel dispatches each makes
 # (a weight quantize is: clear amax target, group amax, outer scales, encode).
-STEP_LAUNCHES = [("quantize_weight_dense", 4), ("quantize_weight_up", 4),
-                 ("quantize_weight_down", 4), ("quantize_rows_dense", 1), ("quantize_rows_moe", 1),
+STEP_LAUNCHES = [("quantize_weight_dense", 3), ("quantize_weight_up", 3),
+                 ("quantize_weight_down", 3), ("quantize_rows_dense", 1), ("quantize_rows_moe", 1),
                  ("gemm_dense", 1), ("grouped_gemm_up", 1), ("requantize_rows_amax_reuse", 1),
                  ("grouped_gemm_down", 1)]
 CALIB_BYTES = 1 << 30
