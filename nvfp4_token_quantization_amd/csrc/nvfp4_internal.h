@@ -40,17 +40,26 @@ __device__ __forceinline__ uint32_t block_amax_bits(const uint4& a, const uint4&
 }
 
 // ------------------------------------------------------------ E4M3 codec --
-// RNE_SAT onto E4M3 (OCP FN, bias 7, max 448) for v >= 0 or +inf.  Values at
-// or above 448 (and NaN) saturate; below 2^-6 the grid is the subnormal step
-// 2^-9 and round-to-nearest-even on v * 2^9 is exact; otherwise the fp32
-// mantissa is rounded to 3 bits with ties to even (a carry moves into the
-// exponent).  Branch-free: all three candidates are formed and one selected.
-__device__ __forceinline__ uint32_t e4m3_encode(float v) {
+// RNE_SAT onto E4M3 (OCP FN, bias 7, max 448) for v >= 0 or +inf: returns
+// the code and stores its exact value in `val`.  Values at or above 448 (and
+// NaN) saturate; below 2^-6 the grid is the subnormal step 2^-9 and
+// round-to-nearest-even on v * 2^9 is exact; otherwise the fp32 mantissa is
+// rounded to 3 bits with ties to even (a carry moves into the exponent), and
+// the rounded fp32 pattern is itself the value.  Branch-free: the candidates
+// are formed and one selected.
+__device__ __forceinline__ uint32_t e4m3_round(float v, float& val) {
   const uint32_t u = __float_as_uint(v);
-  const uint32_t nrm = ((u + 0x7FFFFu + ((u >> 20) & 1u)) >> 20) - (120u << 3);
-  const uint32_t sub = (uint32_t)__builtin_rintf(__builtin_fminf(v, 1.0f) * 512.0f);
-  const uint32_t c = (v < 0.015625f) ? sub : nrm;
-  return (v < 448.0f) ? c : 0x7Eu;
+  const uint32_t r = (u + 0x7FFFFu + ((u >> 20) & 1u)) & 0xFFF00000u;
+  const float sub = __builtin_rintf(__builtin_fminf(v, 1.0f) * 512.0f);
+  const bool is_sub = v < 0.015625f, sat = !(v < 448.0f);
+  val = sat ? 448.0f : (is_sub ? sub * 0.001953125f : __uint_as_float(r));
+  const uint32_t c = is_sub ? (uint32_t)sub : (r >> 20) - (120u << 3);
+  return sat ? 0x7Eu : c;
+}
+
+__device__ __forceinline__ uint32_t e4m3_encode(float v) {
+  float val;
+  return e4m3_round(v, val);
 }
 
 // Exact fp32 value of an E4M3 code 0..0x7E.
@@ -106,8 +115,10 @@ __device__ __forceinline__ void block_scale(uint32_t amax_bits, const RowScale& 
   } else {
     v = ab / rs.t;
   }
-  code = (rs.S == 0.0f) ? 0u : e4m3_encode(v);
-  const float d = rs.S * e4m3_decode(code);
+  float sbv;
+  code = e4m3_round(v, sbv);
+  if (rs.S == 0.0f) code = 0u;
+  const float d = rs.S * sbv;  // S == 0 gives d == 0 whatever sbv is
   const uint32_t db = __float_as_uint(d);
   if (__builtin_expect(db - 0x01000000u < 0x7C000000u - 0x01000000u && (db & 0x7FFFFFu) != 0x7FFFFFu, 1)) {
     const float y0 = __builtin_amdgcn_rcpf(d);

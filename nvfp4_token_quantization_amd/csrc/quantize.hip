@@ -130,17 +130,34 @@ __device__ __forceinline__ void encode_rows(const RowData<U>& r, int64_t rows, i
   if (MODE != MODE_GROUP && row_ok && j == 0) s[row] = rs.S;
   // the group's first row also stores its outer scale (when asked to)
   if (MODE == MODE_GROUP && s && row_ok && j == 0 && row == r.gi * rows_per_group) s[r.gi] = rs.S;
+  // Both lanes of a pair hold the same blocks; for slots (i, i + 1) the even
+  // lane derives block i's scale and the odd lane block i + 1's, and a DPP
+  // swap hands each lane the other result (an odd last slot is derived by
+  // both).  Every lane runs this part, so the swaps see their partners.
+  uint32_t code[U];
+  float inv[U];
+  const bool odd = (j & 1) != 0;
+#pragma unroll
+  for (int i = 0; i + 1 < U; i += 2) {
+    uint32_t c;
+    float v;
+    block_scale(odd ? bmax[i + 1] : bmax[i], rs, c, v);
+    const uint32_t c_p = dpp_mov<0xB1>(c);
+    const float v_p = __uint_as_float(dpp_mov<0xB1>(__float_as_uint(v)));
+    code[i] = odd ? c_p : c;
+    inv[i] = odd ? v_p : v;
+    code[i + 1] = odd ? c : c_p;
+    inv[i + 1] = odd ? v : v_p;
+  }
+  if (U & 1) block_scale(bmax[U - 1], rs, code[U - 1], inv[U - 1]);
   uint32_t* qr = reinterpret_cast<uint32_t*>(q + (row_ok ? row : 0) * (k / 2));
   uint8_t* sr = sb + (row_ok ? row : 0) * (k / 16);
 #pragma unroll
   for (int i = 0; i < U; ++i) {
     const int h = j + L * i;
     if (row_ok && h < nh) {
-      uint32_t code;
-      float inv;
-      block_scale(bmax[i], rs, code, inv);
-      qr[h] = encode_half(r.d[i], inv);
-      if ((j & 1) == 0) sr[h >> 1] = (uint8_t)code;
+      qr[h] = encode_half(r.d[i], inv[i]);
+      if (!odd) sr[h >> 1] = (uint8_t)code[i];
     }
   }
 }
