@@ -150,15 +150,52 @@ __global__ __launch_bounds__(256) void swiglu_quantize_kernel(
       if (amax_out) amax_out[row] = amax;
       if (quantize) s[row] = rs.S;
     }
+    // A block is a quad of lanes, all holding its amax.  Lane d of each quad
+    // derives the scales of slots d, d + 4, ... and quad broadcasts hand them
+    // to the other three lanes (every lane runs this, so the DPP sources are
+    // live; slots past f carry amax 0 and are never stored).
+    uint32_t code_t[T];
+    float inv_t[T];
+    if (quantize) {
+      const int qd = lw & 3;
+#pragma unroll
+      for (int t0 = 0; t0 < T; t0 += 4) {
+        uint32_t a = bmax[t0];
+#pragma unroll
+        for (int d = 1; d < 4; ++d)
+          if (t0 + d < T) a = (qd == d) ? bmax[t0 + d] : a;
+        uint32_t c;
+        float v;
+        block_scale(a, rs, c, v);
+        const uint32_t vb = __float_as_uint(v);
+        code_t[t0] = dpp_mov<0x00>(c);
+        inv_t[t0] = __uint_as_float(dpp_mov<0x00>(vb));
+        if (t0 + 1 < T) {
+          code_t[t0 + 1] = dpp_mov<0x55>(c);
+          inv_t[t0 + 1] = __uint_as_float(dpp_mov<0x55>(vb));
+        }
+        if (t0 + 2 < T) {
+          code_t[t0 + 2] = dpp_mov<0xAA>(c);
+          inv_t[t0 + 2] = __uint_as_float(dpp_mov<0xAA>(vb));
+        }
+        if (t0 + 3 < T) {
+          code_t[t0 + 3] = dpp_mov<0xFF>(c);
+          inv_t[t0 + 3] = __uint_as_float(dpp_mov<0xFF>(vb));
+        }
+      }
+    }
 #pragma unroll
     for (int t = 0; t < T; ++t) {
       const int64_t e0 = 4 * (int64_t)(lw + LANES * t);
       if (e0 >= f) continue;
-      if (h_out) reinterpret_cast<uint2*>(h_out + row * f)[e0 / 4] = make_uint2(hb[t][0], hb[t][1]);
+      if (h_out) {  // streaming stores: H is not read again here
+        uint32_t* hp = reinterpret_cast<uint32_t*>(h_out + row * f + e0);
+        __builtin_nontemporal_store(hb[t][0], hp);
+        __builtin_nontemporal_store(hb[t][1], hp + 1);
+      }
       if (!quantize) continue;
-      uint32_t code;
-      float inv;
-      block_scale(bmax[t], rs, code, inv);
+      const uint32_t code = code_t[t];
+      const float inv = inv_t[t];
       float r[4] = {__uint_as_float(hb[t][0] << 16), __uint_as_float(hb[t][0] & 0xFFFF0000u),
                     __uint_as_float(hb[t][1] << 16), __uint_as_float(hb[t][1] & 0xFFFF0000u)};
       if (__builtin_expect(__builtin_isinf(inv), 0)) {
@@ -235,7 +272,10 @@ extern "C" int nvfp4_swiglu_quantize_rows(const float* gate_up, int64_t rows, in
   if (!kern) return NVFP4_ERROR_UNSUPPORTED_SHAPE;
   const int64_t rpb = 4 / wpr;
   const int64_t need = (rows + rpb - 1) / rpb;
-  const int64_t cap = (int64_t)nvfp4host::num_cus() * 8;
+  // enough blocks for one row group per wave at the shapes of interest: with
+  // no prefetch inside a wave, oversubscription is what overlaps one wave's
+  // loads with another's arithmetic
+  const int64_t cap = (int64_t)nvfp4host::num_cus() * 32;
   dim3 grid((unsigned)(need < cap ? need : cap));
   hipLaunchKernelGGL(kern, grid, dim3(256), 0, (hipStream_t)stream, gate_up, rows, f, h_out,
                      amax_out, q, sb, s);
