@@ -28,8 +28,10 @@ namespace nvfp4 {
 
 enum QuantMode { MODE_ROW = 0, MODE_AMAX_IN = 1, MODE_GROUP = 2 };
 
+// Grid cap in launched waves per SIMD (4-wave blocks, so also blocks per
+// CU); registers allow 4-6 resident, the rest queue behind them.
 #ifndef NVFP4_Q_WAVES_PER_SIMD
-#define NVFP4_Q_WAVES_PER_SIMD 8
+#define NVFP4_Q_WAVES_PER_SIMD 32
 #endif
 
 __device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
@@ -341,8 +343,9 @@ static void launch_rows(const uint16_t* x, int64_t rows, int64_t k, const float*
   int lanes = 0;
   RowKernel kern = pick_row_kernel<MODE>(nh, lanes);
   if (kern) {
-    // enough resident waves to keep HBM busy, and several row groups per wave
-    // so loads overlap encoding (NVFP4_Q_WAVES_PER_SIMD waves per SIMD)
+    // a few row groups per wave at the largest shapes (loads of group i + 1
+    // overlap the encoding of group i), and enough queued waves that one
+    // wave's loads overlap another's arithmetic at the small ones
     const int64_t rows_per_block = 4 * (64 / lanes);
     const int64_t need = (rows + rows_per_block - 1) / rows_per_block;
     const int64_t cap = (int64_t)nvfp4host::num_cus() * NVFP4_Q_WAVES_PER_SIMD;
