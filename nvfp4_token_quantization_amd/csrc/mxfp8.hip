@@ -11,8 +11,12 @@
 // are far under E4M3's smallest step and round to zero either way) and
 // gfx950's pack-convert rounds it to E4M3 (nearest even, sign kept).
 //
-// One thread per 32-element block over the flat [rows, k] tensor: 64 bytes
-// in, 32 + 1 bytes out, consecutive threads on consecutive blocks.
+// Layout: the [rows, k] tensor is a flat run of 16-byte chunks (8 elements);
+// lane l of a wave takes chunks base + l + 64 u (u < U), so every load
+// instruction reads 1 KB contiguous.  A 32-element block is an aligned quad
+// of lanes: two DPP steps give all four lanes the block amax and its scale,
+// each lane converts its 8 elements into 8 bytes (non-temporal stores: the
+// codes are not read again here) and the quad's first lane stores the scale.
 #include "nvfp4_internal.h"
 
 namespace nvfp4 {
@@ -41,31 +45,39 @@ __device__ __forceinline__ uint32_t fp8_encode4(uint32_t w0, uint32_t w1, float 
                            __uint_as_float(w1 & 0xFFFF0000u) * inv);
 }
 
-template <typename IDX>
+template <typename IDX, int U>
 __global__ __launch_bounds__(256) void mxfp8_quantize_kernel(const uint16_t* __restrict__ x,
-                                                             IDX nblocks, uint8_t* __restrict__ q,
+                                                             IDX nchunks, uint8_t* __restrict__ q,
                                                              uint8_t* __restrict__ sc) {
-  const IDX stride = (IDX)gridDim.x * 256;
-  for (IDX b = (IDX)blockIdx.x * 256 + threadIdx.x; b < nblocks; b += stride) {
-    const uint4* xb = reinterpret_cast<const uint4*>(x) + 4 * (int64_t)b;
-    const uint4 v0 = ld_stream(xb), v1 = ld_stream(xb + 1), v2 = ld_stream(xb + 2),
-                v3 = ld_stream(xb + 3);
-    const uint32_t a = max(block_amax_bits(v0, v1), block_amax_bits(v2, v3));
-    const uint32_t code = mx_scale_code(a);
-    const float inv = __uint_as_float((254u - code) << 23);  // 2^-(code - 127)
-    uint4 o0, o1;
-    o0.x = fp8_encode4(v0.x, v0.y, inv);
-    o0.y = fp8_encode4(v0.z, v0.w, inv);
-    o0.z = fp8_encode4(v1.x, v1.y, inv);
-    o0.w = fp8_encode4(v1.z, v1.w, inv);
-    o1.x = fp8_encode4(v2.x, v2.y, inv);
-    o1.y = fp8_encode4(v2.z, v2.w, inv);
-    o1.z = fp8_encode4(v3.x, v3.y, inv);
-    o1.w = fp8_encode4(v3.z, v3.w, inv);
-    uint4* qo = reinterpret_cast<uint4*>(q) + 2 * (int64_t)b;
-    qo[0] = o0;
-    qo[1] = o1;
-    sc[b] = (uint8_t)code;
+  const int lane = threadIdx.x & 63;
+  const IDX step = (IDX)64 * U;
+  const IDX stride = (IDX)gridDim.x * 4 * step;
+  const uint4* x4 = reinterpret_cast<const uint4*>(x);
+  // wave-uniform loop; nchunks is a multiple of 4 and base of 64, so a quad
+  // is either wholly inside the tensor or wholly past its end
+  for (IDX base = ((IDX)blockIdx.x * 4 + (threadIdx.x >> 6)) * step; base < nchunks;
+       base += stride) {
+    uint4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const IDX c = base + lane + 64 * u;
+      v[u] = c < nchunks ? ld_stream(x4 + c) : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const IDX c = base + lane + 64 * u;
+      uint32_t a = half_amax_bits(v[u]);
+      a = max(a, dpp_mov<0xB1>(a));  // quad_perm [1,0,3,2]
+      a = max(a, dpp_mov<0x4E>(a));  // quad_perm [2,3,0,1]
+      const uint32_t code = mx_scale_code(a);
+      const float inv = __uint_as_float((254u - code) << 23);  // 2^-(code - 127)
+      if (c < nchunks) {
+        uint32_t* qo = reinterpret_cast<uint32_t*>(q) + 2 * (int64_t)c;
+        __builtin_nontemporal_store(fp8_encode4(v[u].x, v[u].y, inv), qo);
+        __builtin_nontemporal_store(fp8_encode4(v[u].z, v[u].w, inv), qo + 1);
+        if ((lane & 3) == 0) sc[c >> 2] = (uint8_t)code;
+      }
+    }
   }
 }
 
@@ -89,17 +101,18 @@ extern "C" int nvfp4_mxfp8_quantize_rows(const uint16_t* x_bf16, int64_t rows, i
   if (!aligned(x_bf16, 16) || !aligned(q, 16)) return NVFP4_ERROR_MISALIGNED;
   int st = nvfp4host::check_arch();
   if (st) return st;
-  const int64_t nblocks = rows * (k / 32);
-  const int64_t need = (nblocks + 255) / 256;
-  const int64_t cap = (int64_t)nvfp4host::num_cus() * 16;
+  const int64_t nchunks = rows * (k / 8);  // 16-byte chunks, 4 per block
+  constexpr int U = 4;
+  const int64_t need = (nchunks + 256 * U - 1) / (256 * U);
+  const int64_t cap = (int64_t)nvfp4host::num_cus() * 32;
   dim3 grid((unsigned)(need < cap ? need : cap));
   hipStream_t str = (hipStream_t)stream;
-  if (nblocks < ((int64_t)1 << 31))
-    hipLaunchKernelGGL(nvfp4::mxfp8_quantize_kernel<uint32_t>, grid, dim3(256), 0, str, x_bf16,
-                       (uint32_t)nblocks, q, sc);
+  if (nchunks + (int64_t)grid.x * 256 * U < ((int64_t)1 << 31))
+    hipLaunchKernelGGL((nvfp4::mxfp8_quantize_kernel<uint32_t, U>), grid, dim3(256), 0, str, x_bf16,
+                       (uint32_t)nchunks, q, sc);
   else
-    hipLaunchKernelGGL(nvfp4::mxfp8_quantize_kernel<uint64_t>, grid, dim3(256), 0, str, x_bf16,
-                       (uint64_t)nblocks, q, sc);
+    hipLaunchKernelGGL((nvfp4::mxfp8_quantize_kernel<uint64_t, U>), grid, dim3(256), 0, str, x_bf16,
+                       (uint64_t)nchunks, q, sc);
   return nvfp4host::launch_status();
 }
 

@@ -39,6 +39,15 @@ __device__ __forceinline__ uint32_t block_amax_bits(const uint4& a, const uint4&
   return max((uint32_t)m.x, (uint32_t)m.y);
 }
 
+// max of the 8 bf16 magnitudes held in one uint4 (as a bf16 bit pattern)
+__device__ __forceinline__ uint32_t half_amax_bits(const uint4& a) {
+  const uint32_t M = 0x7FFF7FFFu;
+  const u16x2 m = __builtin_elementwise_max(
+      __builtin_elementwise_max(__builtin_bit_cast(u16x2, a.x & M), __builtin_bit_cast(u16x2, a.y & M)),
+      __builtin_elementwise_max(__builtin_bit_cast(u16x2, a.z & M), __builtin_bit_cast(u16x2, a.w & M)));
+  return max((uint32_t)m.x, (uint32_t)m.y);
+}
+
 // ------------------------------------------------------------ E4M3 codec --
 // RNE_SAT onto E4M3 (OCP FN, bias 7, max 448) for v >= 0 or +inf: returns
 // the code and stores its exact value in `val`.  Values at or above 448 (and

@@ -65,15 +65,6 @@ __device__ __forceinline__ uint32_t encode_half(const uint4& a, float inv) {
   return q;
 }
 
-// Max of the 8 bf16 magnitudes in a uint4 (as a bf16 bit pattern).
-__device__ __forceinline__ uint32_t half_amax_bits(const uint4& a) {
-  const uint32_t M = 0x7FFF7FFFu;
-  const u16x2 m = __builtin_elementwise_max(
-      __builtin_elementwise_max(__builtin_bit_cast(u16x2, a.x & M), __builtin_bit_cast(u16x2, a.y & M)),
-      __builtin_elementwise_max(__builtin_bit_cast(u16x2, a.z & M), __builtin_bit_cast(u16x2, a.w & M)));
-  return max((uint32_t)m.x, (uint32_t)m.y);
-}
-
 // The U half-blocks of one row group held by a lane, and the row's supplied
 // amax (row or group) when there is one.  The amax load is issued before the
 // row's data loads: vector memory counters retire in order, so waiting for
