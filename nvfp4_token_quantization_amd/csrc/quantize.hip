@@ -245,14 +245,16 @@ __global__ __launch_bounds__(256) void fill_zero_kernel(float* __restrict__ p, i
     p[i] = 0.0f;
 }
 
-// Group amax: block (g, c) reduces chunk c of group g's contiguous elements
-// (4 independent 16-byte streaming loads in flight per thread) and folds it
-// into amax[g] with an atomic max on the bit pattern (order independent, so
-// the result is deterministic).
-__global__ __launch_bounds__(256) void group_amax_kernel(const uint16_t* __restrict__ w,
-                                                         int64_t group_elems, int64_t chunk_vecs,
-                                                         int chunks, float* __restrict__ amax) {
-  __shared__ uint32_t red[4];
+// Group amax: block (g, c) of 1024 threads reduces chunk c of group g's
+// contiguous elements (4 independent 16-byte streaming loads in flight per
+// thread) and folds it into amax[g] with an atomic max on the bit pattern
+// (order independent, so the result is deterministic).  Atomics on one
+// address serialize (about 10 ns each), so large blocks keep their number
+// low for a per-tensor scale (groups = 1) at the same wave count.
+__global__ __launch_bounds__(1024) void group_amax_kernel(const uint16_t* __restrict__ w,
+                                                          int64_t group_elems, int64_t chunk_vecs,
+                                                          int chunks, float* __restrict__ amax) {
+  __shared__ uint32_t red[16];
   const int64_t g = blockIdx.x / chunks;
   const int64_t c = blockIdx.x % chunks;
   const int64_t nvec = group_elems / 8;  // 16-byte vectors in the group
@@ -261,17 +263,18 @@ __global__ __launch_bounds__(256) void group_amax_kernel(const uint16_t* __restr
   const int64_t v1 = min(nvec, v0 + chunk_vecs);
   uint32_t m = 0;
   int64_t v = v0 + threadIdx.x;
-  for (; v + 3 * 256 < v1; v += 4 * 256) {
-    uint4 a = ld_stream(base + v), b = ld_stream(base + v + 256);
-    uint4 c2 = ld_stream(base + v + 512), d = ld_stream(base + v + 768);
+  for (; v + 3 * 1024 < v1; v += 4 * 1024) {
+    uint4 a = ld_stream(base + v), b = ld_stream(base + v + 1024);
+    uint4 c2 = ld_stream(base + v + 2048), d = ld_stream(base + v + 3072);
     m = max(m, max(block_amax_bits(a, b), block_amax_bits(c2, d)));
   }
-  for (; v < v1; v += 256) m = max(m, block_amax_bits(base[v], make_uint4(0, 0, 0, 0)));
+  for (; v < v1; v += 1024) m = max(m, block_amax_bits(base[v], make_uint4(0, 0, 0, 0)));
   m = group_max_u32<64>(m);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
   __syncthreads();
   if (threadIdx.x == 0) {
-    uint32_t r = max(max(red[0], red[1]), max(red[2], red[3]));
+    uint32_t r = 0;
+    for (int i = 0; i < 16; ++i) r = max(r, red[i]);
     atomicMax(reinterpret_cast<unsigned int*>(amax + g), r << 16);
   }
 }
@@ -407,14 +410,14 @@ extern "C" int nvfp4_quantize_weight(const uint16_t* w_bf16, int64_t groups, int
                        amax_out, groups);
     const int64_t group_elems = rows_per_group * k;
     if (group_elems > 0) {
-      // large chunks (up to 1 MiB of bf16 per block) keep the reads streaming;
-      // at least ~1024 blocks keep every CU busy
+      // large chunks (256 KiB to 4 MiB of bf16 per block) keep the reads
+      // streaming; about 256 blocks of 16 waves keep every CU busy
       const int64_t nvec = group_elems / 8;
-      int64_t chunk_vecs = (nvec * groups) / 1024;
-      chunk_vecs = chunk_vecs < 4096 ? 4096 : (chunk_vecs > 65536 ? 65536 : chunk_vecs);
+      int64_t chunk_vecs = (nvec * groups) / 256;
+      chunk_vecs = chunk_vecs < 16384 ? 16384 : (chunk_vecs > 262144 ? 262144 : chunk_vecs);
       int64_t chunks = (nvec + chunk_vecs - 1) / chunk_vecs;
       if (chunks * groups > ((int64_t)1 << 30)) return NVFP4_ERROR_UNSUPPORTED_SHAPE;
-      hipLaunchKernelGGL(nvfp4::group_amax_kernel, dim3((unsigned)(chunks * groups)), dim3(256), 0,
+      hipLaunchKernelGGL(nvfp4::group_amax_kernel, dim3((unsigned)(chunks * groups)), dim3(1024), 0,
                          str, w_bf16, group_elems, chunk_vecs, (int)chunks, amax_out);
     }
   }
