@@ -188,7 +188,7 @@ def main():
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path "
+        print("bench.py measures one GPU: the library has no multi-GPU path "
               "(--gpus %d / WORLD_SIZE %d requested)" % (args.gpus, world), file=sys.stderr)
         sys.exit(2)
 
