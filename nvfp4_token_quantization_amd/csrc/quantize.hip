@@ -16,12 +16,16 @@
 //  - A block's two halves sit in lanes 2m and 2m+1: each lane takes the
 //    packed 16-bit max over its 8 bf16 magnitude bits (exact: non-negative
 //    bf16 bit patterns order like their values) and one DPP swap combines
-//    the pair, so both lanes hold the block amax and derive the same scale.
+//    the pair, so both lanes hold the block amax.  Of two slots, the even
+//    lane derives one block's scale and the odd lane the other's, and a
+//    second DPP swap shares the results.
 //  - Row amax: DPP / ds_swizzle / readlane max over the row's lanes.
-//  - Per block one correctly rounded division (a_b / 6S) and one correctly
-//    rounded reciprocal (1 / d); per element one fp32 multiply and half of a
-//    gfx950 pack-convert to E2M1 (two elements per instruction).  Each lane
-//    stores one dword of codes per half-block; even lanes store the scale.
+//  - Per row the correctly rounded S = amax / 2688, t = 6 S and 1 / t; per
+//    block the correctly rounded a_b / t and 1 / d from fma corrections
+//    (block_scale in nvfp4_internal.h); per element one fp32 multiply and
+//    half of a gfx950 pack-convert to E2M1 (two elements per instruction).
+//    Each lane stores one dword of codes per half-block; even lanes store
+//    the scale.
 #include "nvfp4_internal.h"
 
 namespace nvfp4 {
