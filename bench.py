@@ -383,7 +383,8 @@ def main():
     # the in-step figures (which stay the components' numbers)
     b2b = {}
     step0 = dict(launches(0))
-    for n in ("quantize_rows_dense", "quantize_rows_moe", "requantize_rows_amax_reuse"):
+    for n in (() if args.no_next else
+              ("quantize_rows_dense", "quantize_rows_moe", "requantize_rows_amax_reuse")):
         ms = time_extra(step0[n], K)
         ach = work[n][1] / (ms * 1e-3) / 1e9
         b2b[n] = {"ms": round(ms, 4), "GB/s": round(ach, 1), "frac_hbm": round(ach / HBM_PEAK_GBS, 4)}
