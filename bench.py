@@ -92,7 +92,7 @@ def gemm_bytes(a_rows, m_out, n, k, groups):
 
 
 # Launch order of one step and the number of kernel dispatches each makes
-# (a weight quantize is: clear amax target, group amax, outer scales, encode).
+# (a weight quantize is: clear amax target, group amax, encode with scales).
 STEP_LAUNCHES = [("quantize_weight_dense", 3), ("quantize_weight_up", 3),
                  ("quantize_weight_down", 3), ("quantize_rows_dense", 1), ("quantize_rows_moe", 1),
                  ("gemm_dense", 1), ("grouped_gemm_up", 1), ("requantize_rows_amax_reuse", 1),
@@ -133,10 +133,11 @@ def _pmc_dispatches(csv_dir, counter):
     return [(k, v[0], v[1], v[2]) for k, v in sorted(acc.items())]
 
 
-def pmc_summary(fetch_dir, write_dir, cfetch_dir, cwrite_dir):
+def pmc_summary(fetch_dir, write_dir, cfetch_dir, cwrite_dir, path=None):
     """Per-launch HBM bytes of every step launch from FETCH_SIZE and
     WRITE_SIZE runs of this bench, each scaled by the same counter's reading
-    for a plain copy of CALIB_BYTES; writes profiles/traffic.json."""
+    for a plain copy of CALIB_BYTES; writes `path` (default
+    profiles/traffic.json) and returns the summary."""
     out = {"calibration": {}, "kernels": {}}
     per = {}
     for counter, ddir, cdir in (("FETCH_SIZE", fetch_dir, cfetch_dir),
@@ -164,16 +165,19 @@ def pmc_summary(fetch_dir, write_dir, cfetch_dir, cwrite_dir):
         w = sum(d["WRITE_SIZE"]) / len(d["WRITE_SIZE"])
         out["kernels"][name] = {"fetch_bytes": round(f), "write_bytes": round(w),
                                 "bytes_per_launch": round(f + w), "source_digest": kernel_digest(name)}
-    path = os.path.join(ROOT, "profiles", "traffic.json")
-    json.dump(out, open(path, "w"), indent=1)
+    path = path or os.path.join(ROOT, "profiles", "traffic.json")
+    with open(path, "w") as f:
+        json.dump(out, f, indent=1)
     print(json.dumps(out, indent=1))
+    return out
 
 
 def main():
     if len(sys.argv) > 1 and sys.argv[1] == "--calib-copy":
         return calib_copy()
     if len(sys.argv) > 1 and sys.argv[1] == "--pmc-summary":
-        return pmc_summary(*sys.argv[2:6])
+        pmc_summary(*sys.argv[2:6])
+        return None
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
