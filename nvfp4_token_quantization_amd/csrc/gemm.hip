@@ -290,6 +290,288 @@ __global__ __launch_bounds__(64) void gemm_rd_kernel(GemmArgs p) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// LDS-staged variant (k % 128 == 0, 16-byte aligned codes, operands under
+// 2 GiB).  Same wave tile, MFMA layout and K permutation as the
+// register-direct kernel, but every operand byte reaches the wave through a
+// buffer_load ... lds (global -> LDS, no VGPRs) whose lanes read whole 64-byte
+// row segments: four consecutive lanes cover one row's stage, so a 16-row
+// instruction touches 16 segments where the register layout touched 64
+// lane-sized pieces, which the vector L1 serves one by one.  Each wave owns
+// two private LDS stage buffers (no sharing, no barriers); the DMA of stage
+// s + 2 is issued while stage s is consumed, and half-stages move from LDS to
+// registers one half ahead of the MFMAs.
+//
+// The DMA is written as inline asm: the compiler's wait insertion cannot tell
+// the two stage buffers apart and would drain every DMA in flight before each
+// ds_read.  The asm blocks clobber memory, and the waits are explicit:
+// vmcnt before a stage is read, lgkmcnt before its buffer is refilled.
+//
+// LDS stage buffer (per wave): 8 slabs (4 of A, 4 of B) of 32 rows x 64 code
+// bytes, then 8 x 32 rows x 8 scale bytes.  Code row r keeps its four 16-byte
+// chunks XOR-swizzled by (r >> 1) & 3, so the ds_read_b128s of eight
+// consecutive rows hit eight different 16-byte bank groups.
+constexpr int LDS_SLAB_CODES = 32 * 64;
+constexpr int LDS_SLAB_SCALES = 32 * 8;
+constexpr int LDS_SCALES_AT = 8 * LDS_SLAB_CODES;
+constexpr int LDS_STAGE = 8 * (LDS_SLAB_CODES + LDS_SLAB_SCALES);
+constexpr int LDS_EPI = 128 * 4;  // per-row epilogue scales
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ int lds_swz(int r) { return (r >> 1) & 3; }
+
+// Raw buffer resource over `bytes` bytes at p (stride 0; loads whose VGPR
+// offset is at or past `bytes` read nothing).
+__device__ __forceinline__ i32x4 make_rsrc(const void* p, int64_t bytes) {
+  const uint64_t a = (uint64_t)p;
+  return (i32x4){(int)(uint32_t)a, (int)((a >> 32) & 0xFFFFu), (int)bytes, 0x00020000};
+}
+
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+// 16 bytes per lane from rsrc[voff + soff] to LDS[lds + 16 * lane]
+__device__ __forceinline__ void dma16(i32x4 rsrc, uint32_t voff, uint32_t soff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %3\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
+               :: "v"(voff), "s"(rsrc), "s"(soff), "s"(lds) : "memory", "m0");
+}
+// 4 bytes per lane from rsrc[voff + soff] to LDS[lds + 4 * lane]
+__device__ __forceinline__ void dma4(i32x4 rsrc, uint32_t voff, uint32_t soff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %3\n\ts_nop 0\n\tbuffer_load_dword %0, %1, %2 offen lds"
+               :: "v"(voff), "s"(rsrc), "s"(soff), "s"(lds) : "memory", "m0");
+}
+#pragma clang diagnostic pop
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
+}
+__device__ __forceinline__ void wait_lgkmcnt0() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+struct LdsOperands {
+  i32x4 aq, as, bq, bs;
+  uint32_t aoff[4][2], asoff[4], boff[4][2], bsoff[4];
+  uint32_t avalid, bvalid;  // bit i: this lane's MFMA row / column of slab i exists
+};
+
+// DMA of one K stage (k0) into the LDS stage buffer at LDS address `buf`: VS
+// slabs of A, all four of B.  3 VS + 12 instructions.
+template <int VS>
+__device__ __forceinline__ void lds_issue(const LdsOperands& o, uint32_t buf, uint32_t k0) {
+  const uint32_t sc = k0 / 2, ss = k0 / 16;
+#pragma unroll
+  for (int i = 0; i < VS; ++i) {
+    dma16(o.aq, o.aoff[i][0], sc, buf + i * LDS_SLAB_CODES);
+    dma16(o.aq, o.aoff[i][1], sc, buf + i * LDS_SLAB_CODES + 1024);
+    dma4(o.as, o.asoff[i], ss, buf + LDS_SCALES_AT + i * LDS_SLAB_SCALES);
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    dma16(o.bq, o.boff[j][0], sc, buf + (4 + j) * LDS_SLAB_CODES);
+    dma16(o.bq, o.boff[j][1], sc, buf + (4 + j) * LDS_SLAB_CODES + 1024);
+    dma4(o.bs, o.bsoff[j], ss, buf + LDS_SCALES_AT + (4 + j) * LDS_SLAB_SCALES);
+  }
+}
+
+// Half a stage in the MFMA register layout: lane (li, h) holds 16-byte chunk
+// 2h + part of row li (K elements [64h + 32 part, +32)) and the dword of the
+// four block scales of its 64 elements.
+struct RegHalf {
+  uint4 a[4], b[4];
+  uint32_t as[4], bs[4];
+};
+
+// ds_reads of half `part` of the stage at `buf`; rows that do not exist get a
+// zero scale, so they decode to zeros whatever their LDS bytes hold.
+template <int VS>
+__device__ __forceinline__ void lds_read(const LdsOperands& o, const uint8_t* buf, int li, int h,
+                                         int part, RegHalf& r) {
+  const int c = ((2 * h + part) ^ lds_swz(li)) * 16;
+  const uint8_t* sc = buf + LDS_SCALES_AT + li * 8 + 4 * h;
+#pragma unroll
+  for (int i = 0; i < VS; ++i) {
+    r.a[i] = *reinterpret_cast<const uint4*>(buf + i * LDS_SLAB_CODES + li * 64 + c);
+    const uint32_t sv = *reinterpret_cast<const uint32_t*>(sc + i * LDS_SLAB_SCALES);
+    r.as[i] = ((o.avalid >> i) & 1u) ? sv : 0u;
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    r.b[j] = *reinterpret_cast<const uint4*>(buf + (4 + j) * LDS_SLAB_CODES + li * 64 + c);
+    const uint32_t sv = *reinterpret_cast<const uint32_t*>(sc + (4 + j) * LDS_SLAB_SCALES);
+    r.bs[j] = ((o.bvalid >> j) & 1u) ? sv : 0u;
+  }
+}
+
+// Decode of one k-step (dword t of each 16-byte chunk, block scale byte blk)
+template <int VS>
+__device__ __forceinline__ void decode_step(const RegHalf& r, int t, int blk, f16x8 (&fa)[4],
+                                            f16x8 (&fb)[4]) {
+#pragma unroll
+  for (int i = 0; i < VS; ++i) fa[i] = decode8(pick(r.a[i], t), scale_pair(r.as[i], blk));
+#pragma unroll
+  for (int j = 0; j < 4; ++j) fb[j] = decode8(pick(r.b[j], t), scale_pair(r.bs[j], blk));
+}
+
+// One k-step: the MFMAs of the decoded operands (fa, fb) while the next
+// k-step (dword nt, scale byte nblk of `nr`) is decoded, interleaved one MFMA
+// to a few VALU instructions so the decode issues in the MFMAs' shadow.
+template <int VS>
+__device__ __forceinline__ void kstep(f32x16 (&acc)[4][4], f16x8 (&fa)[4], f16x8 (&fb)[4],
+                                      const RegHalf& nr, int nt, int nblk) {
+  f16x8 na[4], nb[4];
+  decode_step<VS>(nr, nt, nblk, na, nb);
+#pragma unroll
+  for (int i = 0; i < VS; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+  constexpr int NM = 4 * VS, NV = ((VS + 4) * 9 + NM - 1) / NM;
+#pragma unroll
+  for (int m = 0; m < NM; ++m) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+    __builtin_amdgcn_sched_group_barrier(0x002, NV, 0);  // then up to NV VALU
+  }
+#pragma unroll
+  for (int i = 0; i < VS; ++i) fa[i] = na[i];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) fb[j] = nb[j];
+}
+
+template <int VS>
+__device__ __forceinline__ void lds_body(const GemmArgs& p, const LdsOperands& o, uint8_t* lds,
+                                         int h, int li, int64_t row_lo, int64_t row_hi, int64_t n0,
+                                         const float* s_rowscale) {
+  constexpr int NI = 3 * VS + 12;  // DMA instructions per stage
+  f32x16 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < VS; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = (f32x16){0};
+  const uint32_t lbase = (uint32_t)(uintptr_t)lds;  // LDS address (low 32 bits)
+  const int nst = (int)(p.k / BK);                   // >= 1 on this path
+  RegHalf r0, r1;
+  f16x8 fa[4], fb[4];
+  lds_issue<VS>(o, lbase, 0);
+  if (nst > 1) {
+    lds_issue<VS>(o, lbase + LDS_STAGE, BK);
+    wait_vmcnt<NI>();
+  } else {
+    wait_vmcnt<0>();
+  }
+  lds_read<VS>(o, lds, li, h, 0, r0);
+  decode_step<VS>(r0, 0, 0, fa, fb);
+  for (int s = 0; s < nst; ++s) {
+    const int cur = s & 1;
+    lds_read<VS>(o, lds + cur * LDS_STAGE, li, h, 1, r1);
+    // k-steps 0..3 from r0; the last one decodes k-step 4 from r1
+    kstep<VS>(acc, fa, fb, r0, 1, 0);
+    kstep<VS>(acc, fa, fb, r0, 2, 1);
+    kstep<VS>(acc, fa, fb, r0, 3, 1);
+    kstep<VS>(acc, fa, fb, r1, 0, 2);
+    // every read of this buffer has been issued; once they land the buffer
+    // takes stage s + 2
+    wait_lgkmcnt0();
+    if (s + 2 < nst) {
+      lds_issue<VS>(o, lbase + cur * LDS_STAGE, (uint32_t)(s + 2) * BK);
+      wait_vmcnt<NI>();  // stage s + 1 is in LDS
+    } else {
+      wait_vmcnt<0>();
+    }
+    if (s + 1 < nst) lds_read<VS>(o, lds + (cur ^ 1) * LDS_STAGE, li, h, 0, r0);
+    // k-steps 4..7 from r1; the last one decodes k-step 0 of stage s + 1
+    // (unused after the last stage)
+    kstep<VS>(acc, fa, fb, r1, 1, 2);
+    kstep<VS>(acc, fa, fb, r1, 2, 3);
+    kstep<VS>(acc, fa, fb, r1, 3, 3);
+    kstep<VS>(acc, fa, fb, r0, 0, 0);
+  }
+  __syncthreads();  // s_rowscale (written by this wave) is visible
+#pragma unroll
+  for (int i = 0; i < VS; ++i) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int lrow = 32 * i + 8 * (r >> 2) + 4 * h + (r & 3);
+      const int64_t row = row_lo + lrow;
+      if (row >= row_hi) continue;
+      const float sc = s_rowscale[lrow];
+      float* yr = p.y + row * p.n;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int64_t col = n0 + 32 * j + li;
+        if (col < p.n) __builtin_nontemporal_store(acc[i][j][r] * sc, yr + col);
+      }
+    }
+  }
+}
+
+__global__ __launch_bounds__(64) void gemm_lds_kernel(GemmArgs p) {
+  constexpr int BM = 128, BN = 128;
+  // two stage buffers, then the epilogue row scales; the expert tile prefix
+  // (read before the K loop only) shares the second stage buffer
+  __shared__ __attribute__((aligned(16))) uint8_t s_lds[2 * LDS_STAGE + LDS_EPI];
+  static_assert((MAX_GROUPS + 1) * 4 <= LDS_STAGE, "tile prefix must fit a stage buffer");
+  int32_t* s_prefix = reinterpret_cast<int32_t*>(s_lds + LDS_STAGE);
+  float* s_rowscale = reinterpret_cast<float*>(s_lds + 2 * LDS_STAGE);
+
+  const int lane = threadIdx.x;
+  const int h = lane >> 5, li = lane & 31;
+
+  TileRange tr;
+  if (!schedule_tile<BM, BN>(p.t, lane, s_prefix, tr)) return;  // block-uniform
+  const int64_t row_lo = tr.row_lo, row_hi = tr.row_hi, n0 = tr.n0;
+  const int g = tr.g;
+  const int64_t rowb = p.k / 2, rows_s = p.k / 16;
+
+  auto a_source = [&](int64_t out_row) -> int64_t {
+    if (out_row >= row_hi) return -1;
+    int64_t r = p.row_index ? (int64_t)p.row_index[out_row] : out_row;
+    return (r >= 0 && r < p.a_rows) ? r : -1;
+  };
+
+  LdsOperands o;
+  o.aq = make_rsrc(p.a_q, p.a_rows * rowb);
+  o.as = make_rsrc(p.a_sb, p.a_rows * rows_s);
+  o.bq = make_rsrc(p.b_q + (int64_t)g * p.n * rowb, p.n * rowb);
+  o.bs = make_rsrc(p.b_sb + (int64_t)g * p.n * rows_s, p.n * rows_s);
+  o.avalid = o.bvalid = 0u;
+  // DMA lanes: codes of row 16u + lane / 4 (chunk (lane & 3) ^ swz), scales of
+  // row lane / 2 (dword lane & 1).  Rows that do not exist get an offset past
+  // the end of the operand, which the buffer range check turns into no read.
+  const uint32_t OOB = 0x80000000u;
+  const int cr = lane >> 2, cc = lane & 3, sr = lane >> 1, sd = lane & 1;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int lr = 16 * u + cr;
+      const uint32_t chunk = (uint32_t)((cc ^ lds_swz(lr)) * 16);
+      const int64_t r = a_source(row_lo + 32 * i + lr);
+      o.aoff[i][u] = r >= 0 ? (uint32_t)(r * rowb) + chunk : OOB;
+      const int64_t c = n0 + 32 * i + lr;
+      o.boff[i][u] = c < p.n ? (uint32_t)(c * rowb) + chunk : OOB;
+    }
+    const int64_t r = a_source(row_lo + 32 * i + sr);
+    o.asoff[i] = r >= 0 ? (uint32_t)(r * rows_s) + 4u * sd : OOB;
+    const int64_t c = n0 + 32 * i + sr;
+    o.bsoff[i] = c < p.n ? (uint32_t)(c * rows_s) + 4u * sd : OOB;
+    if (a_source(row_lo + 32 * i + li) >= 0) o.avalid |= 1u << i;
+    if (n0 + 32 * i + li < p.n) o.bvalid |= 1u << i;
+  }
+  {
+    const float sbw = p.b_s[g];
+    for (int r = lane; r < BM; r += 64) {
+      const int64_t ar = a_source(row_lo + r);
+      s_rowscale[r] = (ar >= 0 ? p.a_s[ar] : 0.0f) * sbw;
+    }
+  }
+  const int vslabs = (int)min((int64_t)4, (row_hi - row_lo + 31) / 32);
+  switch (vslabs) {
+    case 4: lds_body<4>(p, o, s_lds, h, li, row_lo, row_hi, n0, s_rowscale); break;
+    case 3: lds_body<3>(p, o, s_lds, h, li, row_lo, row_hi, n0, s_rowscale); break;
+    case 2: lds_body<2>(p, o, s_lds, h, li, row_lo, row_hi, n0, s_rowscale); break;
+    default: lds_body<1>(p, o, s_lds, h, li, row_lo, row_hi, n0, s_rowscale); break;
+  }
+}
+
 template <int TM, int TN>
 static void launch_gemm_rd(const GemmArgs& a, bool grouped, hipStream_t stream) {
   constexpr int BM = 32 * TM, BN = 32 * TN;
@@ -298,7 +580,13 @@ static void launch_gemm_rd(const GemmArgs& a, bool grouped, hipStream_t stream) 
   const bool fast = (p.k % BK) == 0 && nvfp4host::aligned(p.a_q, 16) &&
                     nvfp4host::aligned(p.b_q, 16) && nvfp4host::aligned(p.a_sb, 4) &&
                     nvfp4host::aligned(p.b_sb, 4);
-  if (fast)
+  // the LDS path addresses operands with 32-bit buffer offsets
+  const int64_t lim = (int64_t)1 << 31;
+  const bool lds_ok = TM == 4 && TN == 4 && p.a_rows > 0 && p.a_rows * (p.k / 2) < lim &&
+                      p.n * (p.k / 2) < lim;
+  if (fast && lds_ok)
+    hipLaunchKernelGGL(gemm_lds_kernel, dim3((unsigned)blocks), dim3(64), 0, stream, p);
+  else if (fast)
     hipLaunchKernelGGL((gemm_rd_kernel<TM, TN, true>), dim3((unsigned)blocks), dim3(64), 0, stream, p);
   else
     hipLaunchKernelGGL((gemm_rd_kernel<TM, TN, false>), dim3((unsigned)blocks), dim3(64), 0, stream, p);
