@@ -291,7 +291,7 @@ __global__ __launch_bounds__(64) void gemm_rd_kernel(GemmArgs p) {
 }
 
 // ---------------------------------------------------------------------------
-// LDS-staged variant (k % 128 == 0, 16-byte aligned codes, operands under
+// LDS-staged variant (k % 256 == 0, 16-byte aligned codes, operands under
 // 2 GiB).  Same wave tile, MFMA layout and K permutation as the
 // register-direct kernel, but every operand byte reaches the wave through a
 // buffer_load ... lds (global -> LDS, no VGPRs) whose lanes read whole 64-byte
@@ -307,15 +307,23 @@ __global__ __launch_bounds__(64) void gemm_rd_kernel(GemmArgs p) {
 // ds_read.  The asm blocks clobber memory, and the waits are explicit:
 // vmcnt before a stage is read, lgkmcnt before its buffer is refilled.
 //
-// LDS stage buffer (per wave): 8 slabs (4 of A, 4 of B) of 32 rows x 64 code
-// bytes, then 8 x 32 rows x 8 scale bytes.  Code row r keeps its four 16-byte
-// chunks XOR-swizzled by (r >> 1) & 3, so the ds_read_b128s of eight
-// consecutive rows hit eight different 16-byte bank groups.
+// LDS per wave (40 KiB, so four one-wave blocks fill a CU's 160 KiB):
+//   two code stage buffers of 8 slabs (4 of A, 4 of B) x 32 rows x 64 bytes;
+//     code row r keeps its four 16-byte chunks XOR-swizzled by (r >> 1) & 3,
+//     so the ds_read_b128s of eight consecutive rows hit eight different
+//     16-byte bank groups;
+//   two scale buffers, each holding a PAIR of stages: 8 slabs x 32 rows x 16
+//     bytes (stage 2p's 8 scale bytes, then stage 2p + 1's), loaded 16 bytes
+//     per lane, so a scale DMA moves 16 bytes per row touched instead of 4.
+// The epilogue's per-row scales reuse the first code buffer after the K loop,
+// and the expert tile prefix (read before the K loop) the second.
 constexpr int LDS_SLAB_CODES = 32 * 64;
-constexpr int LDS_SLAB_SCALES = 32 * 8;
-constexpr int LDS_SCALES_AT = 8 * LDS_SLAB_CODES;
-constexpr int LDS_STAGE = 8 * (LDS_SLAB_CODES + LDS_SLAB_SCALES);
-constexpr int LDS_EPI = 128 * 4;  // per-row epilogue scales
+constexpr int LDS_CODES = 8 * LDS_SLAB_CODES;   // one code stage buffer
+constexpr int LDS_SLAB_SCALES = 32 * 16;
+constexpr int LDS_SCALES = 8 * LDS_SLAB_SCALES;  // one scale pair buffer
+constexpr int LDS_SCALES_AT = 2 * LDS_CODES;
+constexpr int LDS_WAVE = 2 * LDS_CODES + 2 * LDS_SCALES;
+static_assert(LDS_WAVE * 4 <= 160 * 1024, "four waves per CU");
 
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 
@@ -349,27 +357,36 @@ __device__ __forceinline__ void wait_lgkmcnt0() { asm volatile("s_waitcnt lgkmcn
 
 struct LdsOperands {
   i32x4 aq, as, bq, bs;
-  uint32_t aoff[4][2], asoff[4], boff[4][2], bsoff[4];
+  uint32_t aoff[4][2], asoff[2], boff[4][2], bsoff[2];
   uint32_t avalid, bvalid;  // bit i: this lane's MFMA row / column of slab i exists
 };
 
-// DMA of one K stage (k0) into the LDS stage buffer at LDS address `buf`: VS
-// slabs of A, all four of B.  3 VS + 12 instructions.
+// DMA of one K stage's codes (k0) into the code buffer at LDS address `buf`:
+// VS slabs of A, all four of B; 2 VS + 8 instructions.
 template <int VS>
-__device__ __forceinline__ void lds_issue(const LdsOperands& o, uint32_t buf, uint32_t k0) {
-  const uint32_t sc = k0 / 2, ss = k0 / 16;
+__device__ __forceinline__ void lds_issue_codes(const LdsOperands& o, uint32_t buf, uint32_t k0) {
+  const uint32_t sc = k0 / 2;
 #pragma unroll
   for (int i = 0; i < VS; ++i) {
     dma16(o.aq, o.aoff[i][0], sc, buf + i * LDS_SLAB_CODES);
     dma16(o.aq, o.aoff[i][1], sc, buf + i * LDS_SLAB_CODES + 1024);
-    dma4(o.as, o.asoff[i], ss, buf + LDS_SCALES_AT + i * LDS_SLAB_SCALES);
   }
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     dma16(o.bq, o.boff[j][0], sc, buf + (4 + j) * LDS_SLAB_CODES);
     dma16(o.bq, o.boff[j][1], sc, buf + (4 + j) * LDS_SLAB_CODES + 1024);
-    dma4(o.bs, o.bsoff[j], ss, buf + LDS_SCALES_AT + (4 + j) * LDS_SLAB_SCALES);
   }
+}
+
+// DMA of the scales of stages k0 / BK and k0 / BK + 1 into the scale pair
+// buffer at `buf`: one instruction per two slabs (lanes 0-31 the first slab's
+// rows, 32-63 the second's), four instructions.
+__device__ __forceinline__ void lds_issue_scales(const LdsOperands& o, uint32_t buf, uint32_t k0) {
+  const uint32_t ss = k0 / 16;
+  dma16(o.as, o.asoff[0], ss, buf);
+  dma16(o.as, o.asoff[1], ss, buf + 2 * LDS_SLAB_SCALES);
+  dma16(o.bs, o.bsoff[0], ss, buf + 4 * LDS_SLAB_SCALES);
+  dma16(o.bs, o.bsoff[1], ss, buf + 6 * LDS_SLAB_SCALES);
 }
 
 // Half a stage in the MFMA register layout: lane (li, h) holds 16-byte chunk
@@ -380,13 +397,15 @@ struct RegHalf {
   uint32_t as[4], bs[4];
 };
 
-// ds_reads of half `part` of the stage at `buf`; rows that do not exist get a
-// zero scale, so they decode to zeros whatever their LDS bytes hold.
+// ds_reads of half `part` of the stage whose codes are at `buf` and whose
+// scales are the `odd` half of the pair buffer `sbuf`; rows that do not exist
+// get a zero scale, so they decode to zeros whatever their LDS bytes hold.
 template <int VS>
-__device__ __forceinline__ void lds_read(const LdsOperands& o, const uint8_t* buf, int li, int h,
-                                         int part, RegHalf& r) {
+__device__ __forceinline__ void lds_read(const LdsOperands& o, const uint8_t* buf,
+                                         const uint8_t* sbuf, int odd, int li, int h, int part,
+                                         RegHalf& r) {
   const int c = ((2 * h + part) ^ lds_swz(li)) * 16;
-  const uint8_t* sc = buf + LDS_SCALES_AT + li * 8 + 4 * h;
+  const uint8_t* sc = sbuf + li * 16 + 8 * odd + 4 * h;
 #pragma unroll
   for (int i = 0; i < VS; ++i) {
     r.a[i] = *reinterpret_cast<const uint4*>(buf + i * LDS_SLAB_CODES + li * 64 + c);
@@ -438,45 +457,62 @@ __device__ __forceinline__ void kstep(f32x16 (&acc)[4][4], f16x8 (&fa)[4], f16x8
 
 template <int VS>
 __device__ __forceinline__ void lds_body(const GemmArgs& p, const LdsOperands& o, uint8_t* lds,
-                                         int h, int li, int64_t row_lo, int64_t row_hi, int64_t n0,
-                                         const float* s_rowscale) {
-  constexpr int NI = 3 * VS + 12;  // DMA instructions per stage
+                                         int h, int li, int lane, int64_t row_lo, int64_t row_hi,
+                                         int64_t n0, float rs0, float rs1) {
+  constexpr int NC = 2 * VS + 8;  // code DMA instructions per stage
+  constexpr int NS = 4;           // scale DMA instructions per stage pair
   f32x16 acc[4][4];
 #pragma unroll
   for (int i = 0; i < VS; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = (f32x16){0};
   const uint32_t lbase = (uint32_t)(uintptr_t)lds;  // LDS address (low 32 bits)
-  const int nst = (int)(p.k / BK);                   // >= 1 on this path
+  const int nst = (int)(p.k / BK);                   // even and >= 2 on this path
   RegHalf r0, r1;
   f16x8 fa[4], fb[4];
-  lds_issue<VS>(o, lbase, 0);
-  if (nst > 1) {
-    lds_issue<VS>(o, lbase + LDS_STAGE, BK);
-    wait_vmcnt<NI>();
+  // stage s: codes in code buffer s & 1, scales in pair buffer (s >> 1) & 1.
+  // In flight at most: codes of two stages and scales of two pairs.
+  lds_issue_scales(o, lbase + LDS_SCALES_AT, 0);
+  lds_issue_codes<VS>(o, lbase, 0);
+  lds_issue_codes<VS>(o, lbase + LDS_CODES, BK);
+  if (nst > 2) {
+    lds_issue_scales(o, lbase + LDS_SCALES_AT + LDS_SCALES, 2 * BK);
+    wait_vmcnt<NC + NS>();  // stage 0's codes and scales are in LDS
   } else {
-    wait_vmcnt<0>();
+    wait_vmcnt<NC>();
   }
-  lds_read<VS>(o, lds, li, h, 0, r0);
+  lds_read<VS>(o, lds, lds + LDS_SCALES_AT, 0, li, h, 0, r0);
   decode_step<VS>(r0, 0, 0, fa, fb);
   for (int s = 0; s < nst; ++s) {
     const int cur = s & 1;
-    lds_read<VS>(o, lds + cur * LDS_STAGE, li, h, 1, r1);
+    const uint8_t* sbuf = lds + LDS_SCALES_AT + ((s >> 1) & 1) * LDS_SCALES;
+    lds_read<VS>(o, lds + cur * LDS_CODES, sbuf, cur, li, h, 1, r1);
     // k-steps 0..3 from r0; the last one decodes k-step 4 from r1
     kstep<VS>(acc, fa, fb, r0, 1, 0);
     kstep<VS>(acc, fa, fb, r0, 2, 1);
     kstep<VS>(acc, fa, fb, r0, 3, 1);
     kstep<VS>(acc, fa, fb, r1, 0, 2);
-    // every read of this buffer has been issued; once they land the buffer
-    // takes stage s + 2
+    // every read of stage s has been issued; once they land its code buffer
+    // takes stage s + 2, and after an odd stage its scale pair buffer takes
+    // the pair after next (stages s + 3, s + 4).  Stage s + 1 is in LDS once
+    // only this iteration's DMAs can still be in flight.
     wait_lgkmcnt0();
     if (s + 2 < nst) {
-      lds_issue<VS>(o, lbase + cur * LDS_STAGE, (uint32_t)(s + 2) * BK);
-      wait_vmcnt<NI>();  // stage s + 1 is in LDS
+      if (cur && s + 3 < nst) {
+        lds_issue_scales(o, lbase + LDS_SCALES_AT + ((s >> 1) & 1) * LDS_SCALES,
+                         (uint32_t)(s + 3) * BK);
+        lds_issue_codes<VS>(o, lbase + cur * LDS_CODES, (uint32_t)(s + 2) * BK);
+        wait_vmcnt<NC + NS>();
+      } else {
+        lds_issue_codes<VS>(o, lbase + cur * LDS_CODES, (uint32_t)(s + 2) * BK);
+        wait_vmcnt<NC>();
+      }
     } else {
       wait_vmcnt<0>();
     }
-    if (s + 1 < nst) lds_read<VS>(o, lds + (cur ^ 1) * LDS_STAGE, li, h, 0, r0);
+    if (s + 1 < nst)
+      lds_read<VS>(o, lds + (cur ^ 1) * LDS_CODES,
+                   lds + LDS_SCALES_AT + (((s + 1) >> 1) & 1) * LDS_SCALES, cur ^ 1, li, h, 0, r0);
     // k-steps 4..7 from r1; the last one decodes k-step 0 of stage s + 1
     // (unused after the last stage)
     kstep<VS>(acc, fa, fb, r1, 1, 2);
@@ -484,6 +520,12 @@ __device__ __forceinline__ void lds_body(const GemmArgs& p, const LdsOperands& o
     kstep<VS>(acc, fa, fb, r1, 3, 3);
     kstep<VS>(acc, fa, fb, r0, 0, 0);
   }
+  // per-row epilogue scales into the first code buffer (its last reads have
+  // landed: the final k-steps consumed them)
+  float* s_rowscale = reinterpret_cast<float*>(lds);
+  wait_lgkmcnt0();
+  s_rowscale[lane] = rs0;
+  s_rowscale[lane + 64] = rs1;
   __syncthreads();  // s_rowscale (written by this wave) is visible
 #pragma unroll
   for (int i = 0; i < VS; ++i) {
@@ -505,12 +547,9 @@ __device__ __forceinline__ void lds_body(const GemmArgs& p, const LdsOperands& o
 
 __global__ __launch_bounds__(64) void gemm_lds_kernel(GemmArgs p) {
   constexpr int BM = 128, BN = 128;
-  // two stage buffers, then the epilogue row scales; the expert tile prefix
-  // (read before the K loop only) shares the second stage buffer
-  __shared__ __attribute__((aligned(16))) uint8_t s_lds[2 * LDS_STAGE + LDS_EPI];
-  static_assert((MAX_GROUPS + 1) * 4 <= LDS_STAGE, "tile prefix must fit a stage buffer");
-  int32_t* s_prefix = reinterpret_cast<int32_t*>(s_lds + LDS_STAGE);
-  float* s_rowscale = reinterpret_cast<float*>(s_lds + 2 * LDS_STAGE);
+  __shared__ __attribute__((aligned(16))) uint8_t s_lds[LDS_WAVE];
+  static_assert((MAX_GROUPS + 1) * 4 <= LDS_CODES, "tile prefix must fit a code buffer");
+  int32_t* s_prefix = reinterpret_cast<int32_t*>(s_lds + LDS_CODES);
 
   const int lane = threadIdx.x;
   const int h = lane >> 5, li = lane & 31;
@@ -533,11 +572,12 @@ __global__ __launch_bounds__(64) void gemm_lds_kernel(GemmArgs p) {
   o.bq = make_rsrc(p.b_q + (int64_t)g * p.n * rowb, p.n * rowb);
   o.bs = make_rsrc(p.b_sb + (int64_t)g * p.n * rows_s, p.n * rows_s);
   o.avalid = o.bvalid = 0u;
-  // DMA lanes: codes of row 16u + lane / 4 (chunk (lane & 3) ^ swz), scales of
-  // row lane / 2 (dword lane & 1).  Rows that do not exist get an offset past
-  // the end of the operand, which the buffer range check turns into no read.
+  // DMA lanes: codes of row 16u + lane / 4 (chunk (lane & 3) ^ swz); scales
+  // of row lane & 31 of slab 2q + lane / 32 (16 bytes: a stage pair).  Rows
+  // that do not exist get an offset past the end of the operand, which the
+  // buffer range check turns into no read.
   const uint32_t OOB = 0x80000000u;
-  const int cr = lane >> 2, cc = lane & 3, sr = lane >> 1, sd = lane & 1;
+  const int cr = lane >> 2, cc = lane & 3;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
 #pragma unroll
@@ -549,26 +589,28 @@ __global__ __launch_bounds__(64) void gemm_lds_kernel(GemmArgs p) {
       const int64_t c = n0 + 32 * i + lr;
       o.boff[i][u] = c < p.n ? (uint32_t)(c * rowb) + chunk : OOB;
     }
-    const int64_t r = a_source(row_lo + 32 * i + sr);
-    o.asoff[i] = r >= 0 ? (uint32_t)(r * rows_s) + 4u * sd : OOB;
-    const int64_t c = n0 + 32 * i + sr;
-    o.bsoff[i] = c < p.n ? (uint32_t)(c * rows_s) + 4u * sd : OOB;
     if (a_source(row_lo + 32 * i + li) >= 0) o.avalid |= 1u << i;
     if (n0 + 32 * i + li < p.n) o.bvalid |= 1u << i;
   }
-  {
-    const float sbw = p.b_s[g];
-    for (int r = lane; r < BM; r += 64) {
-      const int64_t ar = a_source(row_lo + r);
-      s_rowscale[r] = (ar >= 0 ? p.a_s[ar] : 0.0f) * sbw;
-    }
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int64_t r = a_source(row_lo + 64 * q + lane);
+    o.asoff[q] = r >= 0 ? (uint32_t)(r * rows_s) : OOB;
+    const int64_t c = n0 + 64 * q + lane;
+    o.bsoff[q] = c < p.n ? (uint32_t)(c * rows_s) : OOB;
   }
+  // this lane's two epilogue row scales (rows lane and lane + 64), written to
+  // LDS after the K loop
+  const float sbw = p.b_s[g];
+  const int64_t ar0 = a_source(row_lo + lane), ar1 = a_source(row_lo + 64 + lane);
+  const float rs0 = (ar0 >= 0 ? p.a_s[ar0] : 0.0f) * sbw;
+  const float rs1 = (ar1 >= 0 ? p.a_s[ar1] : 0.0f) * sbw;
   const int vslabs = (int)min((int64_t)4, (row_hi - row_lo + 31) / 32);
   switch (vslabs) {
-    case 4: lds_body<4>(p, o, s_lds, h, li, row_lo, row_hi, n0, s_rowscale); break;
-    case 3: lds_body<3>(p, o, s_lds, h, li, row_lo, row_hi, n0, s_rowscale); break;
-    case 2: lds_body<2>(p, o, s_lds, h, li, row_lo, row_hi, n0, s_rowscale); break;
-    default: lds_body<1>(p, o, s_lds, h, li, row_lo, row_hi, n0, s_rowscale); break;
+    case 4: lds_body<4>(p, o, s_lds, h, li, lane, row_lo, row_hi, n0, rs0, rs1); break;
+    case 3: lds_body<3>(p, o, s_lds, h, li, lane, row_lo, row_hi, n0, rs0, rs1); break;
+    case 2: lds_body<2>(p, o, s_lds, h, li, lane, row_lo, row_hi, n0, rs0, rs1); break;
+    default: lds_body<1>(p, o, s_lds, h, li, lane, row_lo, row_hi, n0, rs0, rs1); break;
   }
 }
 
@@ -582,8 +624,8 @@ static void launch_gemm_rd(const GemmArgs& a, bool grouped, hipStream_t stream) 
                     nvfp4host::aligned(p.b_sb, 4);
   // the LDS path addresses operands with 32-bit buffer offsets
   const int64_t lim = (int64_t)1 << 31;
-  const bool lds_ok = TM == 4 && TN == 4 && p.a_rows > 0 && p.a_rows * (p.k / 2) < lim &&
-                      p.n * (p.k / 2) < lim;
+  const bool lds_ok = TM == 4 && TN == 4 && p.k % 256 == 0 && p.a_rows > 0 &&
+                      p.a_rows * (p.k / 2) < lim && p.n * (p.k / 2) < lim;
   if (fast && lds_ok)
     hipLaunchKernelGGL(gemm_lds_kernel, dim3((unsigned)blocks), dim3(64), 0, stream, p);
   else if (fast)
