@@ -3,8 +3,9 @@ oracle's exact result: |Y - Y_ref| <= 1e-5 * sum_k |a_k b_k| per entry (and
 Y = +-0 where that sum is 0).  Operands are quantized by the oracle, so no
 GEMM input comes from the GPU quantizer.
 
-Small shapes span several tiles, ragged M/N tails and K tails (k % 128 != 0
-takes the masked loader) and are compared in full; the workload shapes are
+Small shapes span several tiles, ragged M/N tails and K tails (k % 256 == 0
+takes the LDS-staged kernel, other multiples of 128 the register-direct one,
+the rest its masked loader) and are compared in full; the workload shapes are
 compared on seeded samples of entries plus whole rows and columns.
 """
 import numpy as np
@@ -33,7 +34,8 @@ def dev_op(t):
 
 @pytest.mark.parametrize("m,n,k", [(1, 1, 16), (3, 5, 32), (37, 53, 512), (128, 128, 128),
                                    (130, 260, 1040), (257, 129, 2048), (64, 384, 2560),
-                                   (300, 200, 784), (65, 1100, 256)])
+                                   (300, 200, 784), (65, 1100, 256), (96, 200, 384),
+                                   (200, 136, 768)])
 def test_dense_small(m, n, k):
     a, b = quant_pair(m * 1000 + n + k, m, n, k)
     y = nv.nvfp4_gemm(dev_op(a), (to_dev(b[0][0]), to_dev(b[1][0]), to_dev(b[2])))
@@ -125,6 +127,7 @@ def grouped_case(seed, tokens, counts, n, k, row_index=True):
     ([0, 0, 257], 64, 2048),
     ([40, 3, 0, 77], 200, 1040),
     ([128, 128, 128], 128, 128),
+    ([3, 70, 0, 129], 160, 384),
 ])
 def test_grouped_small(counts, n, k):
     tokens = 211
