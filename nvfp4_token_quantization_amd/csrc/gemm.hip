@@ -309,9 +309,9 @@ __global__ __launch_bounds__(64) void gemm_rd_kernel(GemmArgs p) {
 //
 // LDS per wave (40 KiB, so four one-wave blocks fill a CU's 160 KiB):
 //   two code stage buffers of 8 slabs (4 of A, 4 of B) x 32 rows x 64 bytes;
-//     code row r keeps its four 16-byte chunks XOR-swizzled by (r >> 1) & 3,
-//     so the ds_read_b128s of eight consecutive rows hit eight different
-//     16-byte bank groups;
+//     code row r keeps its four 16-byte chunks XOR-swizzled by
+//     ((r >> 2) + (r & 2)) & 3, so the ds_read_b128s of any 8 (and any 16)
+//     consecutive rows of an aligned group hit different 16-byte bank groups;
 //   two scale buffers, each holding a PAIR of stages: 8 slabs x 32 rows x 16
 //     bytes (stage 2p's 8 scale bytes, then stage 2p + 1's), loaded 16 bytes
 //     per lane, so a scale DMA moves 16 bytes per row touched instead of 4.
@@ -327,7 +327,7 @@ static_assert(LDS_WAVE * 4 <= 160 * 1024, "four waves per CU");
 
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 
-__device__ __forceinline__ int lds_swz(int r) { return (r >> 1) & 3; }
+__device__ __forceinline__ int lds_swz(int r) { return ((r >> 2) + (r & 2)) & 3; }
 
 // Raw buffer resource over `bytes` bytes at p (stride 0; loads whose VGPR
 // offset is at or past `bytes` read nothing).
