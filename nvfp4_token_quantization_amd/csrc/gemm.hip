@@ -22,15 +22,18 @@
 //       a bias difference of 8, subnormal codes included)
 //   product = e2m1 * s_b = u, exact and normal in fp16.
 //
-// Tiling (measured on MI355X: one wave per SIMD with a 128 x 128 tile and
-// no LDS round trip beats LDS-staged 2x2-wave blocks): one wave per block,
-// the block tile is the wave's 4 x 4 tiles of v_mfma_f32_32x32x16_f16 with
-// 256 fp32 accumulators.  A K stage is 128 elements; lane (li, h) loads, for
-// each 32-row slab of A and B, the 32 code bytes [32h, 32h + 32) of the row's
-// 64 and the dword of the 4 block scales that cover them, one stage ahead into
-// a register double buffer.  Lane half h therefore feeds the K elements
-// [64h, 64h + 64) of every stage to the MFMAs of both operands: a permutation
-// of K that is the same for A and B, so the dot products are unchanged.
+// Tiling: one wave per block (one per SIMD), the block tile is the wave's
+// 4 x 4 tiles of v_mfma_f32_32x32x16_f16 with 256 fp32 accumulators.  A K
+// stage is 128 elements; lane (li, h) holds, for each 32-row slab of A and B,
+// the 32 code bytes [32h, 32h + 32) of the row's 64 and the dword of the 4
+// block scales that cover them, so lane half h feeds the K elements
+// [64h, 64h + 64) of every stage to the MFMAs of both operands: a
+// permutation of K that is the same for A and B, so the dot products are
+// unchanged.  Two ways to get the operands there:
+//   gemm_lds_kernel (k % 256 == 0): global -> private LDS buffers by DMA with
+//     whole row segments per instruction, then ds_reads into that layout;
+//   gemm_rd_kernel (other k): each lane loads its own fragments straight into
+//     a register double buffer.
 //
 // Tile order: blocks are dealt round-robin to the 8 XCDs; the grid is split
 // into 8 regions (one per XCD, along M for grouped GEMMs) so each XCD's L2
