@@ -530,6 +530,31 @@ __device__ __forceinline__ void lds_body(const GemmArgs& p, const LdsOperands& o
   s_rowscale[lane] = rs0;
   s_rowscale[lane + 64] = rs1;
   __syncthreads();  // s_rowscale (written by this wave) is visible
+  // Whole tiles: no per-element checks.  Lane (li, h) holds, for slab i and
+  // accumulator entry 4q + w, row 32i + 8q + 4h + w and column 32j + li; the
+  // four rows' scales come in one 16-byte LDS read, the row address is
+  // wave-uniform and the lane adds 4h rows and li columns.
+  if (row_hi - row_lo >= 128 && n0 + 128 <= p.n && p.n < ((int64_t)1 << 28)) {
+    const int32_t loff = 4 * h * (int32_t)p.n + li;
+    f32x4 sc4[4][4];
+#pragma unroll
+    for (int i = 0; i < VS; ++i)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        sc4[i][q] = *reinterpret_cast<const f32x4*>(s_rowscale + 32 * i + 8 * q + 4 * h);
+#pragma unroll
+    for (int i = 0; i < VS; ++i)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          float* rowp = p.y + (row_lo + 32 * i + 8 * q + w) * p.n + n0;
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            __builtin_nontemporal_store(acc[i][j][4 * q + w] * sc4[i][q][w], rowp + loff + 32 * j);
+        }
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < VS; ++i) {
 #pragma unroll
