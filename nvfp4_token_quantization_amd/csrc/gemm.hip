@@ -352,6 +352,10 @@ __device__ __forceinline__ void dma4(i32x4 rsrc, uint32_t voff, uint32_t soff, u
                :: "v"(voff), "s"(rsrc), "s"(soff), "s"(lds) : "memory", "m0");
 }
 #pragma clang diagnostic pop
+// Streaming 4-byte store to rsrc[voff] (dropped when voff is out of range).
+__device__ __forceinline__ void store_nt(__amdgpu_buffer_rsrc_t rsrc, float v, uint32_t voff) {
+  __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), rsrc, voff, 0, 2);
+}
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
@@ -530,12 +534,20 @@ __device__ __forceinline__ void lds_body(const GemmArgs& p, const LdsOperands& o
   s_rowscale[lane] = rs0;
   s_rowscale[lane + 64] = rs1;
   __syncthreads();  // s_rowscale (written by this wave) is visible
-  // Whole tiles: no per-element checks.  Lane (li, h) holds, for slab i and
+  // Stores through a buffer resource over the tile's rows: the range check
+  // drops rows past the tile's last and a huge offset drops columns past n,
+  // so no store needs a branch.  Lane (li, h) holds, for slab i and
   // accumulator entry 4q + w, row 32i + 8q + 4h + w and column 32j + li; the
-  // four rows' scales come in one 16-byte LDS read, the row address is
-  // wave-uniform and the lane adds 4h rows and li columns.
-  if (row_hi - row_lo >= 128 && n0 + 128 <= p.n && p.n < ((int64_t)1 << 28)) {
-    const int32_t loff = 4 * h * (int32_t)p.n + li;
+  // four rows' scales come in one 16-byte LDS read.
+  if (p.n < ((int64_t)1 << 22)) {
+    const uint32_t nb = (uint32_t)p.n * 4u;  // bytes per output row
+    const __amdgpu_buffer_rsrc_t ry = __builtin_amdgcn_make_buffer_rsrc(
+        p.y + row_lo * p.n, (short)0, (int)((row_hi - row_lo) * p.n * 4), 0x00020000);
+    uint32_t vb[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      vb[j] = (n0 + 32 * j + li < p.n) ? (uint32_t)(4 * h) * nb + (uint32_t)(n0 + 32 * j + li) * 4u
+                                        : 0x80000000u;
     f32x4 sc4[4][4];
 #pragma unroll
     for (int i = 0; i < VS; ++i)
@@ -548,10 +560,10 @@ __device__ __forceinline__ void lds_body(const GemmArgs& p, const LdsOperands& o
       for (int q = 0; q < 4; ++q)
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
-          float* rowp = p.y + (row_lo + 32 * i + 8 * q + w) * p.n + n0;
+          const uint32_t ro = (uint32_t)(32 * i + 8 * q + w) * nb;
 #pragma unroll
           for (int j = 0; j < 4; ++j)
-            __builtin_nontemporal_store(acc[i][j][4 * q + w] * sc4[i][q][w], rowp + loff + 32 * j);
+            store_nt(ry, acc[i][j][4 * q + w] * sc4[i][q][w], vb[j] + ro);
         }
     return;
   }
