@@ -554,6 +554,25 @@ __device__ __forceinline__ void lds_body(const GemmArgs& p, const LdsOperands& o
 #pragma unroll
       for (int q = 0; q < 4; ++q)
         sc4[i][q] = *reinterpret_cast<const f32x4*>(s_rowscale + 32 * i + 8 * q + 4 * h);
+    if (row_hi - row_lo == 128 && n0 + 128 <= p.n) {
+      // whole tile: the row offset is wave-uniform (scalar offset), the
+      // column step an immediate
+      const uint32_t vl = (uint32_t)(4 * h) * nb + (uint32_t)(n0 + li) * 4u;
+#pragma unroll
+      for (int i = 0; i < VS; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            const uint32_t ro = (uint32_t)(32 * i + 8 * q + w) * nb;
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+              __builtin_amdgcn_raw_buffer_store_b32(
+                  __builtin_bit_cast(uint32_t, acc[i][j][4 * q + w] * sc4[i][q][w]), ry, vl + 128 * j,
+                  ro, 2);
+          }
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < VS; ++i)
 #pragma unroll
