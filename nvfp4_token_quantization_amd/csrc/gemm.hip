@@ -238,7 +238,7 @@ __device__ __forceinline__ void rd_body(const GemmArgs& p, const uint8_t* const*
 template <int TM, int TN, bool FAST>
 __global__ __launch_bounds__(64) void gemm_rd_kernel(GemmArgs p) {
   constexpr int BM = 32 * TM, BN = 32 * TN;
-  __shared__ int32_t s_prefix[MAX_GROUPS + 1];
+  __shared__ int32_t s_prefix[SCHED_LDS_WORDS];
   __shared__ float s_rowscale[BM];
 
   const int lane = threadIdx.x;
@@ -617,7 +617,7 @@ __device__ __forceinline__ void lds_body(const GemmArgs& p, const LdsOperands& o
 __global__ __launch_bounds__(64) void gemm_lds_kernel(GemmArgs p) {
   constexpr int BM = 128, BN = 128;
   __shared__ __attribute__((aligned(16))) uint8_t s_lds[LDS_WAVE];
-  static_assert((MAX_GROUPS + 1) * 4 <= LDS_CODES, "tile prefix must fit a code buffer");
+  static_assert(SCHED_LDS_WORDS * 4 <= LDS_CODES, "tile schedule must fit a code buffer");
   int32_t* s_prefix = reinterpret_cast<int32_t*>(s_lds + LDS_CODES);
 
   const int lane = threadIdx.x;

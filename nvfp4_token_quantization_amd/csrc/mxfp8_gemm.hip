@@ -66,7 +66,7 @@ __device__ __forceinline__ int mxl_swz(int r) { return ((r >> 1) & 7) ^ ((r & 1)
 
 template <bool FULL>
 __global__ __launch_bounds__(256) void mxfp8_gemm_lds_kernel(MxGemmArgs p) {
-  __shared__ int32_t s_prefix[MAX_GROUPS + 1];
+  __shared__ int32_t s_prefix[SCHED_LDS_WORDS];
   __shared__ uint4 s_a[2][MXL_BM * MXL_BK / 16];
   __shared__ uint4 s_b[2][MXL_BN * MXL_BK / 16];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;

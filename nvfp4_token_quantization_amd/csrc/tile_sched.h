@@ -8,6 +8,10 @@
 namespace nvfp4 {
 
 constexpr int MAX_GROUPS = 1024;
+// int32 words of LDS schedule_tile needs: the expert m-tile prefix, then each
+// expert's clamped row range [lo, hi) (so the block's expert bounds come from
+// LDS, not from a second dependent read of the offsets in memory)
+constexpr int SCHED_LDS_WORDS = 3 * (MAX_GROUPS + 1);
 
 // What the mapping needs: the output rows (dense) or the device offsets of a
 // contiguous per-expert layout (grouped), and the host's launch plan.
@@ -35,7 +39,8 @@ struct TileRange {
 // Returns false when the block has no tile (block-uniform).  Called by the
 // whole block (one wave of 64 lanes).
 template <int BM, int BN>
-__device__ __forceinline__ bool schedule_tile(const TileGrid& t, int lane, int32_t* s_prefix,
+__device__ __forceinline__ bool schedule_tile(const TileGrid& t, int lane,
+                                              int32_t* s_prefix /* SCHED_LDS_WORDS */,
                                               TileRange& out) {
   constexpr int GPT = MAX_GROUPS / 64;
   const int xcd = blockIdx.x % 8;
@@ -70,6 +75,8 @@ __device__ __forceinline__ bool schedule_tile(const TileGrid& t, int lane, int32
   int g = 0;
   if (t.offsets) {
     const int G = t.groups;
+    uint32_t* s_lo = reinterpret_cast<uint32_t*>(s_prefix + (MAX_GROUPS + 1));
+    uint32_t* s_hi = reinterpret_cast<uint32_t*>(s_prefix + 2 * (MAX_GROUPS + 1));
     int32_t local = 0;
     int32_t cnt[GPT];
 #pragma unroll
@@ -80,6 +87,8 @@ __device__ __forceinline__ bool schedule_tile(const TileGrid& t, int lane, int32
         int64_t lo = min(max((int64_t)t.offsets[gg], (int64_t)0), t.m_total);
         int64_t hi = min(max((int64_t)t.offsets[gg + 1], lo), t.m_total);
         c = (int32_t)((hi - lo + BM - 1) / BM);
+        s_lo[gg] = (uint32_t)lo;  // m_total <= 2^31
+        s_hi[gg] = (uint32_t)hi;
       }
       cnt[i] = c;
       local += c;
@@ -110,8 +119,8 @@ __device__ __forceinline__ bool schedule_tile(const TileGrid& t, int lane, int32
       if (s_prefix[mid] <= mt) lo = mid; else hi = mid - 1;
     }
     g = lo;
-    const int64_t glo = min(max((int64_t)t.offsets[g], (int64_t)0), t.m_total);
-    const int64_t ghi = min(max((int64_t)t.offsets[g + 1], glo), t.m_total);
+    const int64_t glo = (int64_t)s_lo[g];
+    const int64_t ghi = (int64_t)s_hi[g];
     row_lo = glo + (mt - s_prefix[g]) * BM;
     row_hi = min(ghi, row_lo + BM);
   } else {
