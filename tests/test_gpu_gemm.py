@@ -60,6 +60,32 @@ def test_dense_all_scale_codes_random_codes():
     check_gemm(y, y_ref, bound, "random codes")
 
 
+def test_dense_very_wide_output():
+    """n >= 2^22 takes the LDS kernel's per-element epilogue (the buffer-store
+    epilogue needs the tile's output bytes under 2^31); a 40-column tail past
+    2^22 and every column near the end are compared, plus random entries."""
+    m, n, k = 3, (1 << 22) + 40, 256
+    rnd = lambda s, shape, hi: (sg.uniform(s, 1, int(np.prod(shape))) * hi).astype(np.int64).reshape(shape)
+    aq = rnd(11, (m, k // 2), 256).astype(np.uint8)
+    asb = rnd(12, (m, k // 16), 0x7F).astype(np.uint8)
+    as_ = np.array([0.5, 3.0, 0.0078125], np.float32)
+    # B: a 4096-row random block repeated down the rows (distinct bytes per
+    # 4096 columns are enough to place every output), then the tail rows
+    blk_q = rnd(13, (4096, k // 2), 256).astype(np.uint8)
+    blk_s = (0x28 + rnd(14, (4096, k // 16), 0x20)).astype(np.uint8)
+    reps = n // 4096 + 1
+    bq = np.tile(blk_q, (reps, 1))[:n]
+    bsb = np.tile(blk_s, (reps, 1))[:n]
+    bs = np.array([0.25], np.float32)
+    y = to_np(nv.nvfp4_gemm((to_dev(aq), to_dev(asb), to_dev(as_)), (to_dev(bq), to_dev(bsb), to_dev(bs))))
+    cnt = 20000
+    ii = np.concatenate([(sg.uniform(15, 1, cnt) * m).astype(np.int64), np.repeat(np.arange(m), 300)])
+    jj = np.concatenate([(sg.uniform(15, 2, cnt) * n).astype(np.int64),
+                         np.tile(np.arange(n - 300, n), m)])
+    y_ref, bound = oracle.gemm_entries((aq, asb, as_), (bq, bsb, bs), ii, jj, np.zeros_like(ii))
+    check_gemm(y[ii, jj], y_ref, bound, "dense %dx%dx%d" % (m, n, k))
+
+
 def test_dense_k0_and_zero_scales():
     m, n = 5, 7
     e = lambda *s: torch.empty(s, dtype=torch.uint8, device=dev())
