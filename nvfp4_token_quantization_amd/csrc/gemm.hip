@@ -341,14 +341,11 @@ __device__ __forceinline__ i32x4 make_rsrc(const void* p, int64_t bytes) {
 
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
-// 16 bytes per lane from rsrc[voff + soff] to LDS[lds + 16 * lane]
+// 16 bytes per lane from rsrc[voff + soff] to LDS[lds + 16 * lane] (the
+// operand rows, scale rows included, are 16-byte aligned: k % 256 == 0 and
+// 16-byte aligned base pointers)
 __device__ __forceinline__ void dma16(i32x4 rsrc, uint32_t voff, uint32_t soff, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %3\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
-               :: "v"(voff), "s"(rsrc), "s"(soff), "s"(lds) : "memory", "m0");
-}
-// 4 bytes per lane from rsrc[voff + soff] to LDS[lds + 4 * lane]
-__device__ __forceinline__ void dma4(i32x4 rsrc, uint32_t voff, uint32_t soff, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %3\n\ts_nop 0\n\tbuffer_load_dword %0, %1, %2 offen lds"
                :: "v"(voff), "s"(rsrc), "s"(soff), "s"(lds) : "memory", "m0");
 }
 #pragma clang diagnostic pop
