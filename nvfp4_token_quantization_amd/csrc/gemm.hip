@@ -535,9 +535,9 @@ __device__ __forceinline__ void lds_body(const GemmArgs& p, const LdsOperands& o
     kstep<VS>(acc, fa, fb, r1, 3, 3);
     kstep<VS>(acc, fa, fb, r0, 0, 0);
   }
-  // per-row epilogue scales into the first code buffer (its last reads have
-  // landed: the final k-steps consumed them)
-  float* s_rowscale = reinterpret_cast<float*>(lds);
+  // per-row epilogue scales into the last 512 bytes of LDS (every read of
+  // the K loop has landed: the final k-steps consumed them)
+  float* s_rowscale = reinterpret_cast<float*>(lds + LDS_WAVE - 512);
   wait_lgkmcnt0();
   s_rowscale[lane] = rs0;
   s_rowscale[lane + 64] = rs1;
@@ -561,6 +561,38 @@ __device__ __forceinline__ void lds_body(const GemmArgs& p, const LdsOperands& o
 #pragma unroll
       for (int q = 0; q < 4; ++q)
         sc4[i][q] = *reinterpret_cast<const f32x4*>(s_rowscale + 32 * i + 8 * q + 4 * h);
+    if ((p.n & 3) == 0) {
+      // Through LDS, so every store writes 16 bytes and a store instruction
+      // covers two whole 512-byte row segments: slab by slab, the scaled
+      // values go to LDS rows of 544 bytes (the 32-byte pad puts the lane
+      // halves' rows on disjoint banks), then lane L reads 16 bytes of row
+      // 2t + L / 32 and stores them.  Four times fewer store instructions than
+      // one value per lane, so the wave rarely stalls on its count of
+      // outstanding memory operations.
+      constexpr int RS = 544;
+      float* t = reinterpret_cast<float*>(lds);
+      const int rr = lane >> 5, cc = lane & 31;
+      const int64_t col = n0 + 4 * cc;
+      const uint32_t vc = col < p.n ? (uint32_t)col * 4u : 0x80000000u;
+#pragma unroll
+      for (int i = 0; i < VS; ++i) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+          for (int w = 0; w < 4; ++w)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+              t[((8 * q + 4 * h + w) * RS + (32 * j + li) * 4) / 4] = acc[i][j][4 * q + w] * sc4[i][q][w];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+          const int r = 2 * u + rr;
+          const f32x4 v = *reinterpret_cast<const f32x4*>(reinterpret_cast<const uint8_t*>(t) + r * RS + cc * 16);
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), ry,
+                                                 vc + (uint32_t)(32 * i + r) * nb, 0, 2);
+        }
+      }
+      return;
+    }
     if (row_hi - row_lo == 128 && n0 + 128 <= p.n) {
       // whole tile: the row offset is wave-uniform (scalar offset), the
       // column step an immediate
