@@ -353,17 +353,6 @@ __device__ __forceinline__ void dma16(i32x4 rsrc, uint32_t voff, uint32_t soff, 
 __device__ __forceinline__ void store_nt(__amdgpu_buffer_rsrc_t rsrc, float v, uint32_t voff) {
   __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), rsrc, voff, 0, 2);
 }
-// Raw buffer resource over `bytes` bytes of the output at p, built from
-// wave-uniform (readfirstlane) values so stores through it need no per-lane
-// resource loop.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t out_rsrc(float* p, int64_t bytes) {
-  const uint64_t a = (uint64_t)p;
-  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
-  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
-  const int num = __builtin_amdgcn_readfirstlane((int)bytes);
-  return __builtin_amdgcn_make_buffer_rsrc((void*)(((uint64_t)hi << 32) | lo), (short)0, num,
-                                           0x00020000);
-}
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");

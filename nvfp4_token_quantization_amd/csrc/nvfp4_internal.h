@@ -173,6 +173,21 @@ __device__ __forceinline__ uint32_t group_max_u32(uint32_t v) {
   return v;
 }
 
+// Raw buffer resource over `bytes` bytes of the output at p (stride 0;
+// accesses whose offset is at or past `bytes` are dropped), built from
+// wave-uniform (readfirstlane) values so accesses through it need no
+// per-lane resource loop.  readfirstlane returns int: the halves are kept as
+// uint32 so the low word is zero-extended, never sign-extended, into the
+// 64-bit base.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t out_rsrc(float* p, int64_t bytes) {
+  const uint64_t a = (uint64_t)p;
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  const int num = __builtin_amdgcn_readfirstlane((int)bytes);
+  return __builtin_amdgcn_make_buffer_rsrc((void*)(((uint64_t)hi << 32) | lo), (short)0, num,
+                                           0x00020000);
+}
+
 }  // namespace nvfp4
 
 // ------------------------------------------------------------- host side --
