@@ -382,16 +382,115 @@ def main():
         torch.cuda.synchronize()
         return a.elapsed_time(b) / iters
 
-    # the per-token quantizers are short enough that an event pair around each
-    # launch adds a visible share; their back-to-back rate is reported beside
-    # the in-step figures (which stay the components' numbers)
-    b2b = {}
-    step0 = dict(launches(0))
-    for n in (() if args.no_next else
-              ("quantize_rows_dense", "quantize_rows_moe", "requantize_rows_amax_reuse")):
-        ms = time_extra(step0[n], K)
-        ach = work[n][1] / (ms * 1e-3) / 1e9
-        b2b[n] = {"ms": round(ms, 4), "GB/s": round(ach, 1), "frac_hbm": round(ach / HBM_PEAK_GBS, 4)}
+    # Rotated-input protocol for the HBM-bound launches timed on their own:
+    # R copies of the inputs (and outputs) with R x footprint >= 1 GiB and
+    # >= 4x the 256 MB MALL, launched round-robin between two events; 3 warm-up
+    # passes, then the median of 10 passes, per launch.
+    ROT_BYTES = max(1 << 30, 4 * 256 * 10**6)
+
+    def rotations(footprint):
+        return max(2, -(-ROT_BYTES // int(footprint)))
+
+    def time_rotated(fns, loops=10, warm=3):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        for _ in range(warm):
+            for f in fns:
+                st = f()
+                if st != 0:
+                    raise RuntimeError("rotated launch failed: %s" % nv.status_string(st))
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(loops):
+            a.record(stream)
+            for f in fns:
+                f()
+            b.record(stream)
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b) / len(fns))
+        return float(np.median(ts))
+
+    rot = {}
+    if not args.no_next:
+        for name, src, amax, rows, kk in (("quantize_rows_dense", X2[0], None, M2, K2),
+                                         ("quantize_rows_moe", X3[0], None, T3, K3),
+                                         ("requantize_rows_amax_reuse", H4[0], H4A[0], MH, K4)):
+            R = rotations(work[name][1])
+            sets = []
+            for _ in range(R):
+                sets.append((src.clone(), None if amax is None else amax.clone(),
+                             empty((rows, kk // 2), u8), empty((rows, kk // 16), u8), empty((rows,), f32)))
+            fns = [(lambda x=x, am=am, q=q, sb=sb, sc=sc: L.nvfp4_quantize_rows(
+                p(x), rows, kk, None if am is None else p(am), p(q), p(sb), p(sc), sp))
+                for x, am, q, sb, sc in sets]
+            ms = time_rotated(fns)
+            ach = work[name][1] / (ms * 1e-3) / 1e9
+            rot[name] = {"ms": round(ms, 4), "GB/s": round(ach, 1), "frac_hbm": round(ach / HBM_PEAK_GBS, 4),
+                         "bytes": int(work[name][1]), "input_sets": R}
+            del sets, fns
+            torch.cuda.empty_cache()
+        log("quantizers, rotated inputs: %s" % rot)
+
+    # Rollout-decode skinny shapes (64 tokens): dense 64 x 2560 -> 9728 and
+    # the MoE up / down projections over the tokens' top-8 routing (512
+    # routed rows, most experts 0-4 rows).  Weight-bandwidth-bound: the
+    # algorithmic bytes count the weights of the experts that receive rows
+    # (E_act, from the routing), the activations and the fp32 outputs.  The
+    # weights are the step's quantized tensors (same shapes and distribution),
+    # copied so the rotation covers >= 1 GiB.
+    decode = {}
+    if not args.no_next:
+        d5 = sg.workload(5, part={"x", "h", "xd", "logits"})
+        xq5 = nv.nvfp4_quantize_rows(up(d5["x"]))
+        hq5 = nv.nvfp4_quantize_rows(up(d5["h"]), amax_in=up(d5["h_amax"]))
+        xdq5 = nv.nvfp4_quantize_rows(up(d5["xd"]))
+        rt5 = nv.nvfp4_moe_route(up(d5["logits"]), 8)
+        off5 = rt5["offsets"]
+        ri5 = rt5["row_index"]
+        torch.cuda.synchronize()
+        counts5 = np.diff(off5.cpu().numpy())   # host copy for the byte accounting only
+        e_act = int((counts5 > 0).sum())
+        MD = xdq5[0].shape[0]
+        MR5 = int(ri5.numel())
+        cases = {
+            "decode_gemm_dense": dict(
+                w=(out["w2"][0][0], out["w2"][1][0], out["w2"][2]), n=N2, k=K2, m_out=MD,
+                bytes=N2 * (K2 // 2 + K2 // 16) + 4 + MD * (K2 // 2 + K2 // 16 + 4) + MD * N2 * 4,
+                flop=2.0 * MD * N2 * K2),
+            "decode_grouped_gemm_up": dict(
+                w=out["w3"][:3], n=N3, k=K3, m_out=MR5,
+                bytes=e_act * (N3 * (K3 // 2 + K3 // 16) + 4) + MR5 * (K3 // 2 + K3 // 16 + 4) + MR5 * N3 * 4,
+                flop=2.0 * MR5 * N3 * K3),
+            "decode_grouped_gemm_down": dict(
+                w=out["w4"][:3], n=N4, k=K4, m_out=MR5,
+                bytes=e_act * (N4 * (K4 // 2 + K4 // 16) + 4) + MR5 * (K4 // 2 + K4 // 16 + 4) + MR5 * N4 * 4,
+                flop=2.0 * MR5 * N4 * K4),
+        }
+        for name, c in cases.items():
+            wfoot = sum(t.numel() * t.element_size() for t in c["w"])
+            R = rotations(wfoot)
+            sets = [(tuple(t.clone() for t in c["w"]), empty((c["m_out"], c["n"]), f32)) for _ in range(R)]
+            if name == "decode_gemm_dense":
+                fns = [(lambda w=w, y=y: L.nvfp4_gemm(
+                    p(xdq5[0]), p(xdq5[1]), p(xdq5[2]), MD, p(w[0]), p(w[1]), p(w[2]), N2, K2, p(y), sp))
+                    for w, y in sets]
+            elif name == "decode_grouped_gemm_up":
+                fns = [(lambda w=w, y=y: L.nvfp4_grouped_gemm(
+                    p(xq5[0]), p(xq5[1]), p(xq5[2]), xq5[0].shape[0], p(ri5), MR5, p(off5), E,
+                    p(w[0]), p(w[1]), p(w[2]), N3, K3, p(y), sp)) for w, y in sets]
+            else:
+                fns = [(lambda w=w, y=y: L.nvfp4_grouped_gemm(
+                    p(hq5[0]), p(hq5[1]), p(hq5[2]), MR5, None, MR5, p(off5), E,
+                    p(w[0]), p(w[1]), p(w[2]), N4, K4, p(y), sp)) for w, y in sets]
+            ms = time_rotated(fns)
+            gbs = c["bytes"] / (ms * 1e-3) / 1e9
+            decode[name] = {"ms": round(ms, 4), "GB/s": round(gbs, 1), "frac_hbm": round(gbs / HBM_PEAK_GBS, 4),
+                            "bytes": int(c["bytes"]), "TFLOP/s": round(c["flop"] / (ms * 1e-3) / 1e12, 2),
+                            "weight_sets": R}
+            del sets, fns
+            torch.cuda.empty_cache()
+        decode["routing"] = {"tokens": MD, "routed_rows": MR5, "experts_with_rows": e_act,
+                             "max_rows_per_expert": int(counts5.max())}
+        log("decode (skinny) shapes: %s" % decode)
 
     if not args.no_next:
         # SwiGLU -> per-token requantize chained on the step's own up-GEMM output
@@ -455,34 +554,49 @@ def main():
         del mx_x2, mx_w2, mx_x3, mx_w3
         log("next rows: %s" % nxt)
 
-    # dominant kernel = longest per step
-    dom = max(names, key=lambda n: per_kernel_ms[n])
-    kind, amount = work[dom]
-    t = per_kernel_ms[dom] * 1e-3
-    if kind == "hbm":
-        roof = {"bound": "hbm", "achieved": round(amount / t / 1e9, 1), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s"}
-    else:
-        roof = {"bound": "mfma", "achieved": round(amount / t / 1e12, 1), "peak": MFMA_F16_PEAK_TFS,
-                "unit": "TFLOP/s"}
+    # Dominant kernel: the kernel function with the most time per step.  The
+    # three GEMM launches all run gemm_lds_kernel (about half the step); the
+    # weight quantizers are three dispatches each (fill, group amax, encode).
+    # Its roofline figure is the launches' algorithmic flops over their
+    # event-timed durations (= mean flops per launch / mean launch time).
+    gemm_names = ("gemm_dense", "grouped_gemm_up", "grouped_gemm_down")
+    t_gemm = sum(per_kernel_ms[n] for n in gemm_names) * 1e-3
+    fl_gemm = sum(work[n][1] for n in gemm_names)
+    roof = {"bound": "mfma", "achieved": round(fl_gemm / t_gemm / 1e12, 1), "peak": MFMA_F16_PEAK_TFS,
+            "unit": "TFLOP/s"}
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
-    roof["kernel"] = dom
-    roof["ms_per_launch"] = round(per_kernel_ms[dom], 4)
+    roof["kernel"] = "gemm_lds_kernel"
+    roof["launches_per_step"] = len(gemm_names)
+    roof["ms_per_launch"] = round(t_gemm * 1e3 / len(gemm_names), 4)
+    roof["flop_per_launch"] = fl_gemm / len(gemm_names)
+    roof["launches"] = {n: {"ms": comps[n]["ms"], "TFLOP/s": comps[n]["TFLOP/s"],
+                            "frac": comps[n]["frac_mfma"]} for n in gemm_names}
     roof["traffic"] = None
+    # the longest HBM-bound launch, with the same fields
+    hdom = max((n for n in names if work[n][0] == "hbm"), key=lambda n: per_kernel_ms[n])
+    t = per_kernel_ms[hdom] * 1e-3
+    roof_hbm = {"bound": "hbm", "achieved": round(work[hdom][1] / t / 1e9, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "kernel": hdom, "ms_per_launch": round(per_kernel_ms[hdom], 4),
+                "traffic": None}
+    roof_hbm["frac"] = round(roof_hbm["achieved"] / HBM_PEAK_GBS, 4)
     tfile = os.path.join(ROOT, "profiles", "traffic.json")
     if os.path.exists(tfile):
         try:
-            tr = json.load(open(tfile))
-            ent = tr.get("kernels", {}).get(dom)
-            if ent and ent.get("source_digest") == kernel_digest(dom):
-                roof["traffic"] = ent["bytes_per_launch"]
+            tr = json.load(open(tfile)).get("kernels", {})
+            ents = [tr.get(n) for n in gemm_names]
+            if all(e and e.get("source_digest") == kernel_digest(n) for e, n in zip(ents, gemm_names)):
+                roof["traffic"] = round(sum(e["bytes_per_launch"] for e in ents) / len(ents))
+            e = tr.get(hdom)
+            if e and e.get("source_digest") == kernel_digest(hdom):
+                roof_hbm["traffic"] = e["bytes_per_launch"]
         except (ValueError, KeyError):
             pass
 
     # headline halves of the metric: the largest per-token quantize and the
     # large grouped GEMM
-    qbest = max(("quantize_rows_dense", "quantize_rows_moe", "requantize_rows_amax_reuse"),
-                key=lambda n: comps[n]["GB/s"])
+    qnames = ("quantize_rows_dense", "quantize_rows_moe", "requantize_rows_amax_reuse")
+    qsrc = rot if rot else comps
+    qbest = max(qnames, key=lambda n: qsrc[n]["GB/s"])
 
     res = {
         "metric": "NVFP4 quantize GB/s + block-scaled grouped GEMM TFLOP/s, % of MI355X peak",
@@ -506,15 +620,19 @@ def main():
             "step_gemm_flop": step_flops,
         },
         "headline": {
-            "quantize_rows_GB/s": comps[qbest]["GB/s"], "quantize_rows_kernel": qbest,
-            "quantize_rows_frac_hbm": comps[qbest]["frac_hbm"],
-            "quantize_rows_back_to_back": b2b,
+            "quantize_rows_GB/s": qsrc[qbest]["GB/s"], "quantize_rows_kernel": qbest,
+            "quantize_rows_frac_hbm": qsrc[qbest]["frac_hbm"],
+            "quantize_rows_protocol": ("rotated inputs >= 1 GiB, median of 10 passes" if rot
+                                       else "in-step event times"),
+            "quantize_rows_rotated": rot,
             "grouped_gemm_up_TFLOP/s": comps["grouped_gemm_up"]["TFLOP/s"],
             "grouped_gemm_up_frac_mfma": comps["grouped_gemm_up"]["frac_mfma"],
         },
         "components": comps,
+        "decode_skinny": decode,
         "next_rows": nxt,
         "roofline": roof,
+        "roofline_hbm": roof_hbm,
         "cpu_baseline": None,
     }
 
@@ -575,10 +693,33 @@ def cpu_baseline(args, work):
         t_step += dt * (work[name][1] / (2.0 * k)) / NE
     step_flops = sum(v[1] for v in work.values() if v[0] == "mfma")
     log("cpu baseline: %.1f s per step (extrapolated)" % t_step)
+    # the per-token quantizer on one thread and on all, same sample (the
+    # dense activation's first R rows), in GB/s of its algorithmic bytes
+    xs = d2["x"][:R]
+    qbytes = quant_rows_bytes(xs.shape[0], xs.shape[1])
+    qrate = {}
+    for nthr in (1, cores):
+        oracle.set_threads(nthr)
+        t = time.time()
+        oracle.quantize_rows(xs)
+        qrate[nthr] = qbytes / (time.time() - t) / 1e9
+    oracle.set_threads(cores)
     return {"value": step_flops / t_step / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
-            "s_per_step": round(t_step, 2),
+            "cpu_model": cpu_model(), "s_per_step": round(t_step, 2),
+            "quantize_rows_GB/s": {"threads_1": round(qrate[1], 4), "threads_%d" % cores: round(qrate[cores], 4)},
             "sample": "oracle on the first %d rows of each quantizer input (weights: %d rows of one "
-                      "group) and %d output entries per GEMM, times scaled to one full step" % (R, R, NE)}
+                      "group) and %d output entries per GEMM, times scaled to one full step; the "
+                      "quantizer rate on %d rows of the dense activation" % (R, R, NE, R)}
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 if __name__ == "__main__":

@@ -113,6 +113,35 @@ def _dev(t, name, dtypes, ndim=None):
 _BF16 = (torch.bfloat16, torch.int16, torch.uint16)
 
 
+def _out(t, name, shape, dtype, device):
+    """Check a caller-supplied output tensor: the kernels write exactly
+    `shape` elements of `dtype` through its pointer, so anything else (a
+    smaller or strided buffer, another device) is refused."""
+    _dev(t, name, (dtype,))
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError("%s must have shape %s (got %s)" % (name, tuple(shape), tuple(t.shape)))
+    if t.device != device:
+        raise ValueError("%s must be on %s (got %s)" % (name, device, t.device))
+    return t
+
+
+def _out_rows(t, name, min_rows, cols, dtype, device):
+    """Output of a grouped GEMM: [rows >= min_rows, cols]; the kernels write
+    only rows below offsets[groups] <= min_rows, so a taller buffer is fine."""
+    _dev(t, name, (dtype,), 2)
+    if t.shape[0] < min_rows or t.shape[1] != cols:
+        raise ValueError("%s must have shape (>= %d, %d) (got %s)" % (name, min_rows, cols, tuple(t.shape)))
+    if t.device != device:
+        raise ValueError("%s must be on %s (got %s)" % (name, device, t.device))
+    return t
+
+
+def _same_device(device, *named):
+    for name, t in named:
+        if t is not None and t.device != device:
+            raise ValueError("%s must be on %s (got %s)" % (name, device, t.device))
+
+
 def nvfp4_quantize_rows(x, amax_in=None, out=None):
     """Per-token NVFP4 of bf16 rows x [rows, k] (k % 16 == 0).
 
@@ -128,10 +157,14 @@ def nvfp4_quantize_rows(x, amax_in=None, out=None):
         s = torch.empty((rows,), dtype=torch.float32, device=dev)
     else:
         q, sb, s = out
+        _out(q, "out q", (rows, k // 2), torch.uint8, dev)
+        _out(sb, "out sb", (rows, k // 16), torch.uint8, dev)
+        _out(s, "out s", (rows,), torch.float32, dev)
     if amax_in is not None:
         _dev(amax_in, "amax_in", (torch.float32,), 1)
         if amax_in.numel() != rows:
             raise ValueError("amax_in must have one entry per row")
+        _same_device(dev, ("amax_in", amax_in))
     st = lib().nvfp4_quantize_rows(_ptr(x), rows, k, _ptr(amax_in), _ptr(q), _ptr(sb), _ptr(s),
                                    _stream(dev))
     _check("nvfp4_quantize_rows", st)
@@ -154,20 +187,18 @@ def nvfp4_swiglu_quantize_rows(gate_up, want_h=False, want_amax=False, quantize=
     dev = gate_up.device
     out = dict(out or {})
     res = {}
+    want = []
     if want_h:
-        res["h"] = out.get("h", None)
-        if res["h"] is None:
-            res["h"] = torch.empty((rows, f), dtype=torch.bfloat16, device=dev)
+        want.append(("h", (rows, f), torch.bfloat16))
     if want_amax:
-        res["amax"] = out.get("amax", None)
-        if res["amax"] is None:
-            res["amax"] = torch.empty((rows,), dtype=torch.float32, device=dev)
+        want.append(("amax", (rows,), torch.float32))
     if quantize:
-        for key, shape, dt in (("q", (rows, f // 2), torch.uint8), ("sb", (rows, f // 16), torch.uint8),
-                               ("s", (rows,), torch.float32)):
-            res[key] = out.get(key, None)
-            if res[key] is None:
-                res[key] = torch.empty(shape, dtype=dt, device=dev)
+        want += [("q", (rows, f // 2), torch.uint8), ("sb", (rows, f // 16), torch.uint8),
+                 ("s", (rows,), torch.float32)]
+    for key, shape, dt in want:
+        t = out.get(key, None)
+        res[key] = torch.empty(shape, dtype=dt, device=dev) if t is None else \
+            _out(t, "out " + key, shape, dt, dev)
     st = lib().nvfp4_swiglu_quantize_rows(_ptr(gate_up), rows, f, _ptr(res.get("h")),
                                           _ptr(res.get("amax")), _ptr(res.get("q")),
                                           _ptr(res.get("sb")), _ptr(res.get("s")), _stream(dev))
@@ -188,8 +219,12 @@ def nvfp4_dequantize_rows(q, sb, s, rows_per_scale=1, out=None):
         raise ValueError("sb must hold k/16 scale codes per row")
     if s.numel() * rows_per_scale < rows:
         raise ValueError("s must hold one outer scale per rows_per_scale rows")
+    _same_device(q.device, ("sb", sb), ("s", s))
+    shape = tuple(q.shape[:-1]) + (k,)
     if out is None:
-        out = torch.empty(tuple(q.shape[:-1]) + (k,), dtype=torch.bfloat16, device=q.device)
+        out = torch.empty(shape, dtype=torch.bfloat16, device=q.device)
+    else:
+        _out(out, "out", shape, torch.bfloat16, q.device)
     st = lib().nvfp4_dequantize_rows(_ptr(q), _ptr(sb), _ptr(s), rows, k, int(rows_per_scale),
                                      _ptr(out), _stream(q.device))
     _check("nvfp4_dequantize_rows", st)
@@ -206,6 +241,8 @@ def nvfp4_mxfp8_quantize_rows(x, out=None):
         sc = torch.empty((rows, k // 32), dtype=torch.uint8, device=x.device)
     else:
         q, sc = out
+        _out(q, "out q", (rows, k), torch.uint8, x.device)
+        _out(sc, "out sc", (rows, k // 32), torch.uint8, x.device)
     st = lib().nvfp4_mxfp8_quantize_rows(_ptr(x), rows, k, _ptr(q), _ptr(sc), _stream(x.device))
     _check("nvfp4_mxfp8_quantize_rows", st)
     return q, sc
@@ -214,13 +251,15 @@ def nvfp4_mxfp8_quantize_rows(x, out=None):
 def nvfp4_mxfp8_gemm(a, b, out=None):
     """Y = deq(A) . deq(B)^T for MXFP8 operands a = (q [m, k], sc [m, k/32]),
     b = (q [n, k], sc [n, k/32]); fp32 [m, n]."""
-    aq, asc = a
-    bq, bsc = b
-    for t, nm in ((aq, "a_q"), (asc, "a_sc"), (bq, "b_q"), (bsc, "b_sc")):
-        _dev(t, nm, (torch.uint8,))
-    m, k = aq.shape[0], aq.shape[-1]
+    aq, asc = _mx_operand(a, "a", 2)
+    bq, bsc = _mx_operand(b, "b", 2)
+    m, k = aq.shape
     n = bq.shape[0]
-    y = out if out is not None else torch.empty((m, n), dtype=torch.float32, device=aq.device)
+    if bq.shape[1] != k:
+        raise ValueError("A and B must have the same k")
+    _same_device(aq.device, ("b.q", bq))
+    y = _out(out, "out", (m, n), torch.float32, aq.device) if out is not None else \
+        torch.empty((m, n), dtype=torch.float32, device=aq.device)
     st = lib().nvfp4_mxfp8_gemm(_ptr(aq), _ptr(asc), m, _ptr(bq), _ptr(bsc), n, k, _ptr(y),
                                 _stream(aq.device))
     _check("nvfp4_mxfp8_gemm", st)
@@ -231,13 +270,18 @@ def nvfp4_mxfp8_grouped_gemm(a, offsets, b, row_index=None, m_total=None, out=No
     """Grouped MXFP8 GEMM: a = (q [a_rows, k], sc [a_rows, k/32]); offsets
     int32 [groups+1] on the device; b = (q [groups, n, k], sc [groups, n,
     k/32]); row_index optional int32 [m_total]."""
-    aq, asc = a
-    bq, bsc = b
+    aq, asc = _mx_operand(a, "a", 2)
+    bq, bsc = _mx_operand(b, "b", 3)
     _dev(offsets, "offsets", (torch.int32,), 1)
     groups, n, k = bq.shape[0], bq.shape[1], bq.shape[2]
-    if m_total is None:
-        m_total = row_index.numel() if row_index is not None else aq.shape[0]
-    y = out if out is not None else torch.empty((m_total, n), dtype=torch.float32, device=aq.device)
+    if aq.shape[1] != k:
+        raise ValueError("A and B must have the same k")
+    if offsets.numel() != groups + 1:
+        raise ValueError("offsets must have groups + 1 entries")
+    m_total = _grouped_rows(aq.shape[0], row_index, m_total)
+    _same_device(aq.device, ("b.q", bq), ("offsets", offsets), ("row_index", row_index))
+    y = _out_rows(out, "out", m_total, n, torch.float32, aq.device) if out is not None else \
+        torch.empty((m_total, n), dtype=torch.float32, device=aq.device)
     st = lib().nvfp4_mxfp8_grouped_gemm(_ptr(aq), _ptr(asc), aq.shape[0], _ptr(row_index), m_total,
                                         _ptr(offsets), groups, _ptr(bq), _ptr(bsc), n, k, _ptr(y),
                                         _stream(aq.device))
@@ -258,9 +302,9 @@ def nvfp4_moe_route(logits, topk, out=None):
     res = {}
     for key, shape in (("experts", (T, topk)), ("offsets", (E + 1,)), ("row_index", (T * topk,)),
                        ("slot_of", (T, topk))):
-        res[key] = out.get(key, None)
-        if res[key] is None:
-            res[key] = torch.empty(shape, dtype=i32, device=dev)
+        t = out.get(key, None)
+        res[key] = torch.empty(shape, dtype=i32, device=dev) if t is None else \
+            _out(t, "out " + key, shape, i32, dev)
     st = lib().nvfp4_moe_route(_ptr(logits), T, E, int(topk), _ptr(res["experts"]),
                                _ptr(res["offsets"]), _ptr(res["row_index"]), _ptr(res["slot_of"]),
                                _stream(dev))
@@ -284,35 +328,84 @@ def nvfp4_quantize_weight(w, amax_in=None, out=None):
         amax = torch.empty((g,), dtype=torch.float32, device=dev)
     else:
         q, sb, s, amax = out
+        _out(q, "out q", (g, r, k // 2), torch.uint8, dev)
+        _out(sb, "out sb", (g, r, k // 16), torch.uint8, dev)
+        _out(s, "out s", (g,), torch.float32, dev)
+        _out(amax, "out amax", (g,), torch.float32, dev)
     if amax_in is not None:
         _dev(amax_in, "amax_in", (torch.float32,), 1)
         if amax_in.numel() != g:
             raise ValueError("amax_in must have one entry per group")
+        _same_device(dev, ("amax_in", amax_in))
     st = lib().nvfp4_quantize_weight(_ptr(w), g, r, k, _ptr(amax_in), _ptr(amax), _ptr(q),
                                      _ptr(sb), _ptr(s), _stream(dev))
     _check("nvfp4_quantize_weight", st)
     return q, sb, s, amax
 
 
-def _operand(t, name):
+def _operand(t, name, ndim, scales):
+    """Check an NVFP4 operand (q, sb, s): q [..., k/2] and sb [..., k/16]
+    with the same leading shape (ndim dims), s with `scales` entries, all on
+    one device."""
     q, sb, s = t
-    _dev(q, name + ".q", (torch.uint8,))
-    _dev(sb, name + ".sb", (torch.uint8,))
+    _dev(q, name + ".q", (torch.uint8,), ndim)
+    _dev(sb, name + ".sb", (torch.uint8,), ndim)
     _dev(s, name + ".s", (torch.float32,))
+    if tuple(sb.shape[:-1]) != tuple(q.shape[:-1]) or sb.shape[-1] * 8 != q.shape[-1]:
+        raise ValueError("%s.sb must be %s + [k/16] for %s.q of shape %s (got %s)" % (
+            name, tuple(q.shape[:-1]), name, tuple(q.shape), tuple(sb.shape)))
+    if s.numel() != scales:
+        raise ValueError("%s.s must have %d entries (got %d)" % (name, scales, s.numel()))
+    _same_device(q.device, (name + ".sb", sb), (name + ".s", s))
     return q, sb, s
+
+
+def _mx_operand(t, name, ndim):
+    """Check an MXFP8 operand (q [..., k], sc [..., k/32])."""
+    q, sc = t
+    _dev(q, name + ".q", (torch.uint8,), ndim)
+    _dev(sc, name + ".sc", (torch.uint8,), ndim)
+    if tuple(sc.shape[:-1]) != tuple(q.shape[:-1]) or sc.shape[-1] * 32 != q.shape[-1]:
+        raise ValueError("%s.sc must be %s + [k/32] for %s.q of shape %s (got %s)" % (
+            name, tuple(q.shape[:-1]), name, tuple(q.shape), tuple(sc.shape)))
+    _same_device(q.device, (name + ".sc", sc))
+    return q, sc
+
+
+def _grouped_rows(a_rows, row_index, m_total):
+    """Output rows of a grouped GEMM: m_total, else len(row_index), else
+    a_rows; checks row_index covers them (or, without it, that A does)."""
+    if row_index is not None:
+        _dev(row_index, "row_index", (torch.int32,), 1)
+        if m_total is None:
+            m_total = row_index.numel()
+        elif row_index.numel() < m_total:
+            raise ValueError("row_index must have m_total entries")
+    elif m_total is None:
+        m_total = a_rows
+    elif m_total > a_rows:
+        raise ValueError("without row_index, A must have at least m_total rows")
+    return int(m_total)
 
 
 def nvfp4_gemm(a, b, out=None):
     """Y = deq(A) . deq(B)^T, fp32 [m, n].  a = (q [m, k/2], sb [m, k/16],
     s [m]); b = (q [n, k/2], sb [n, k/16], s [1])."""
-    aq, asb, as_ = _operand(a, "a")
-    bq, bsb, bs = _operand(b, "b")
-    m, n = aq.shape[0], bq.shape[-2] if bq.dim() == 3 else bq.shape[0]
+    aq = a[0]
+    m = aq.shape[0]
+    aq, asb, as_ = _operand(a, "a", 2, m)
+    bq = b[0]
+    if bq.dim() == 3 and bq.shape[0] == 1:  # a per-tensor weight from nvfp4_quantize_weight
+        b = (bq[0], b[1][0] if b[1].dim() == 3 else b[1], b[2])
+    bq, bsb, bs = _operand(b, "b", 2, 1)
+    n = bq.shape[0]
     k = aq.shape[-1] * 2
     if bq.shape[-1] * 2 != k:
         raise ValueError("A and B must have the same k")
     dev = aq.device
-    y = torch.empty((m, n), dtype=torch.float32, device=dev) if out is None else out
+    _same_device(dev, ("b.q", bq))
+    y = torch.empty((m, n), dtype=torch.float32, device=dev) if out is None else \
+        _out(out, "out", (m, n), torch.float32, dev)
     st = lib().nvfp4_gemm(_ptr(aq), _ptr(asb), _ptr(as_), m, _ptr(bq), _ptr(bsb), _ptr(bs), n, k,
                           _ptr(y), _stream(dev))
     _check("nvfp4_gemm", st)
@@ -328,25 +421,22 @@ def nvfp4_grouped_gemm(a, offsets, b, row_index=None, m_total=None, out=None):
     m_total defaults to len(row_index) or a_rows (the host never reads
     offsets).  Rows at or past offsets[groups] of the output are not written.
     """
-    aq, asb, as_ = _operand(a, "a")
-    bq, bsb, bs = _operand(b, "b")
-    _dev(offsets, "offsets", (torch.int32,), 1)
-    if bq.dim() != 3:
+    aq, asb, as_ = _operand(a, "a", 2, a[0].shape[0] if a[0].dim() == 2 else -1)
+    if b[0].dim() != 3:
         raise ValueError("b.q must be [groups, n, k/2]")
+    bq, bsb, bs = _operand(b, "b", 3, b[0].shape[0])
+    _dev(offsets, "offsets", (torch.int32,), 1)
     groups, n, k = bq.shape[0], bq.shape[1], bq.shape[2] * 2
+    if aq.shape[1] * 2 != k:
+        raise ValueError("A and B must have the same k")
     if offsets.numel() != groups + 1:
         raise ValueError("offsets must have groups + 1 entries")
     a_rows = aq.shape[0]
-    if row_index is not None:
-        _dev(row_index, "row_index", (torch.int32,), 1)
-        if m_total is None:
-            m_total = row_index.numel()
-        elif row_index.numel() < m_total:
-            raise ValueError("row_index must have m_total entries")
-    elif m_total is None:
-        m_total = a_rows
+    m_total = _grouped_rows(a_rows, row_index, m_total)
     dev = aq.device
-    y = torch.empty((m_total, n), dtype=torch.float32, device=dev) if out is None else out
+    _same_device(dev, ("b.q", bq), ("offsets", offsets), ("row_index", row_index))
+    y = torch.empty((m_total, n), dtype=torch.float32, device=dev) if out is None else \
+        _out_rows(out, "out", m_total, n, torch.float32, dev)
     st = lib().nvfp4_grouped_gemm(_ptr(aq), _ptr(asb), _ptr(as_), a_rows, _ptr(row_index),
                                   m_total, _ptr(offsets), groups, _ptr(bq), _ptr(bsb), _ptr(bs),
                                   n, k, _ptr(y), _stream(dev))

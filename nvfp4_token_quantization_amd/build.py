@@ -1,7 +1,9 @@
-"""Build libnvfp4.so (HIP, gfx950) in-tree with hipcc."""
+"""Build libnvfp4.so (HIP, gfx950) in-tree with hipcc: one object per source,
+compiled in parallel, then linked into the shared library."""
 import os
 import subprocess
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
@@ -13,7 +15,7 @@ SOURCES = ["abi_common.hip", "quantize.hip", "swiglu_quantize.hip", "route.hip",
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [
-    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     # correctly rounded fp32 division and reciprocal, denormals kept, no
     # fast-math: the quantizer's fp32 steps are part of its contract
     "-fno-fast-math", "-ffp-contract=off", "-fhip-fp32-correctly-rounded-divide-sqrt",
@@ -24,22 +26,52 @@ FLAGS = [
 ]
 
 
-def build(verbose=False):
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [HIPCC] + FLAGS + ["-I", os.path.join(ROOT, "include"), "-I", CSRC] + srcs + ["-o", tmp]
+def _filter(out):
+    # the host pass does not know the packed-fp32 feature and says so
+    return "\n".join(l for l in out.splitlines() if "packed-fp32-ops" not in l and l.strip())
+
+
+def _run(cmd):
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    return r.returncode, _filter(r.stdout + r.stderr)
+
+
+def build(verbose=False, sources=None, lib=None, jobs=None):
+    """Compile `sources` (default: every source of the library) and link them
+    into `lib` (default: libnvfp4.so next to this file)."""
+    sources = sources or SOURCES
+    lib = lib or LIB
+    objdir = os.path.join(HERE, "_build")
+    os.makedirs(objdir, exist_ok=True)
+    inc = ["-I", os.path.join(ROOT, "include"), "-I", CSRC]
+    tag = "%d" % os.getpid()
+    jobs = jobs or min(len(sources), int(os.environ.get("MAX_JOBS", "8")), os.cpu_count() or 1)
+
+    def compile_one(src):
+        obj = os.path.join(objdir, os.path.splitext(src)[0] + "." + tag + ".o")
+        cmd = [HIPCC] + FLAGS + inc + ["-c", os.path.join(CSRC, src), "-o", obj]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        rc, msg = _run(cmd)
+        return src, obj, rc, msg
+
+    with ThreadPoolExecutor(max_workers=jobs) as ex:
+        results = list(ex.map(compile_one, sources))
+    failed = [(s, m) for s, _, rc, m in results if rc != 0]
+    if failed:
+        raise RuntimeError("hipcc failed:\n" + "\n".join("%s:\n%s" % f for f in failed))
+    objs = [o for _, o, _, _ in results]
+    tmp = lib + ".tmp" + tag
+    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC"] + objs + ["-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
-    r = subprocess.run(cmd, capture_output=True, text=True)
-    # the host pass does not know the packed-fp32 feature and says so
-    msg = "\n".join(l for l in (r.stdout + r.stderr).splitlines()
-                    if "packed-fp32-ops" not in l and l.strip())
-    if r.returncode != 0:
-        raise RuntimeError("hipcc failed:\n" + msg)
-    if msg and verbose:
-        print(msg)
-    os.replace(tmp, LIB)
-    return LIB
+    rc, msg = _run(cmd)
+    for o in objs:
+        os.remove(o)
+    if rc != 0:
+        raise RuntimeError("link failed:\n" + msg)
+    os.replace(tmp, lib)
+    return lib
 
 
 if __name__ == "__main__":

@@ -572,6 +572,7 @@ __device__ __forceinline__ void lds_body(const GemmArgs& p, const LdsOperands& o
 #pragma unroll
             for (int j = 0; j < 4; ++j)
               t[((8 * q + 4 * h + w) * RS + (32 * j + li) * 4) / 4] = acc[i][j][4 * q + w] * sc4[i][q][w];
+        wave_lds_sync();  // the slab's values are in LDS for every lane
 #pragma unroll
         for (int u = 0; u < 16; ++u) {
           const int r = 2 * u + rr;
@@ -579,6 +580,7 @@ __device__ __forceinline__ void lds_body(const GemmArgs& p, const LdsOperands& o
           __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), ry,
                                                  vc + (uint32_t)(32 * i + r) * nb, 0, 2);
         }
+        wave_lds_sync();  // the slab's reads are done before the next slab's writes
       }
       return;
     }

@@ -173,6 +173,17 @@ __device__ __forceinline__ uint32_t group_max_u32(uint32_t v) {
   return v;
 }
 
+// Orders one wave's LDS accesses around an exchange of values between its
+// lanes: every LDS write before the call is visible to every lane's LDS reads
+// after it, and reads before the call complete before later writes.  (A
+// wave's LDS operations already execute in order; this keeps the compiler
+// from reordering them across the exchange.)
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 // Raw buffer resource over `bytes` bytes of the output at p (stride 0;
 // accesses whose offset is at or past `bytes` are dropped), built from
 // wave-uniform (readfirstlane) values so accesses through it need no

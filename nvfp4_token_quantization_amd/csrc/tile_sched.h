@@ -106,6 +106,9 @@ __device__ __forceinline__ bool schedule_tile(const TileGrid& t, int lane,
       if (gg <= G) s_prefix[gg] = run;
       run += cnt[i];
     }
+    // the loop covers entries 0..MAX_GROUPS - 1; with G == MAX_GROUPS the
+    // total (entry G) is the last lane's final running sum
+    if (G == MAX_GROUPS && lane == 63) s_prefix[MAX_GROUPS] = run;
     __syncthreads();
     const int64_t total_mt = s_prefix[G];
     const int64_t mpx = (total_mt + XM - 1) / XM;
@@ -136,8 +139,8 @@ __device__ __forceinline__ bool schedule_tile(const TileGrid& t, int lane,
   if (hf >= 0) {  // half tile: rows [row_lo + (BM/2) hf, row_lo + (BM/2)(hf + 1))
     row_lo += (BM / 2) * hf;
     row_hi = min(row_hi, row_lo + BM / 2);
-    if (row_lo >= row_hi) return false;  // block-uniform
   }
+  if (row_lo >= row_hi) return false;  // block-uniform (never for a consistent prefix)
   out.row_lo = row_lo;
   out.row_hi = row_hi;
   out.n0 = nt * BN;

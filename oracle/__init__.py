@@ -66,6 +66,8 @@ def lib():
         P = ctypes.c_void_p
         I64 = ctypes.c_int64
         L.oracle_threads.restype = ctypes.c_int
+        L.oracle_set_threads.argtypes = [ctypes.c_int]
+        L.oracle_set_threads.restype = None
         L.oracle_e2m1_value.argtypes = [ctypes.c_int]
         L.oracle_e2m1_value.restype = ctypes.c_double
         L.oracle_e4m3_value.argtypes = [ctypes.c_int]
@@ -109,6 +111,11 @@ def _c(a, dtype):
 def threads():
     """OpenMP threads the oracle's parallel loops use."""
     return lib().oracle_threads()
+
+
+def set_threads(n):
+    """Set the OpenMP thread count of the oracle's parallel loops."""
+    lib().oracle_set_threads(int(n))
 
 
 # ------------------------------------------------------------------ codecs --

@@ -55,8 +55,10 @@
 #endif
 #define MUT(k) (ORACLE_MUTANT == (k))
 
-/* number of OpenMP threads the parallel loops below use */
+/* number of OpenMP threads the parallel loops below use, and a way to set it
+ * (the CPU baseline times the quantizer on one thread as well as on all) */
 int oracle_threads(void) { return omp_get_max_threads(); }
+void oracle_set_threads(int n) { omp_set_num_threads(n > 0 ? n : 1); }
 
 /* ---------------------------------------------------------------- codecs -- */
 

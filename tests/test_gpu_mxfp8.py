@@ -205,5 +205,12 @@ def test_mxfp8_gemm_errors():
     d = dev()
     z = torch.zeros((4, 48), dtype=torch.uint8, device=d)
     zs = torch.zeros((4, 1), dtype=torch.uint8, device=d)
-    with pytest.raises(nv.NVFP4Error):
-        nv.nvfp4_mxfp8_gemm((z, zs), (z, zs))    # k = 48 is not a multiple of 32
+    # k = 48 is not a multiple of 32: the binding finds no scale shape for it,
+    # and the library itself returns UNSUPPORTED_SHAPE
+    with pytest.raises(ValueError):
+        nv.nvfp4_mxfp8_gemm((z, zs), (z, zs))
+    y = torch.empty((4, 4), dtype=torch.float32, device=d)
+    sp = torch.cuda.current_stream(d).cuda_stream
+    st = nv.lib().nvfp4_mxfp8_gemm(z.data_ptr(), zs.data_ptr(), 4, z.data_ptr(), zs.data_ptr(), 4, 48,
+                                   y.data_ptr(), sp)
+    assert st == 2
