@@ -28,22 +28,22 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "nvfp4_oracle.c")
 _LIB = os.path.join(_HERE, "libnvfp4_oracle.so")
-# an alternative build of the same source (the mutation tests load builds
-# with one planted mistake each); used as given, never rebuilt here
+# an alternative build (the mutation tests load builds of patched copies of
+# the source, each with one planted mistake); used as given, never rebuilt here
 _LIB_OVERRIDE = os.environ.get("NVFP4_ORACLE_LIB")
 
 GCC_FLAGS = ["-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp", "-ffp-contract=off",
              "-fno-fast-math", "-fexcess-precision=standard", "-Wall"]
+SOURCE = _SRC
 
 
-def build(force=False, mutant=0, path=None):
-    """Compile the oracle with gcc (plain C, IEEE fp32, OpenMP).  `mutant`
-    plants one of the deliberate mistakes of the mutation tests (0: none);
-    `path` overrides the output file."""
-    if mutant or path:
-        out = path or (_LIB + ".mut%d" % mutant)
-        subprocess.check_call(["gcc"] + GCC_FLAGS + ["-DORACLE_MUTANT=%d" % mutant, _SRC, "-o", out,
-                                                    "-lm"])
+def build(force=False, src=None, path=None, extra_flags=()):
+    """Compile the oracle with gcc (plain C, IEEE fp32, OpenMP).  `src` and
+    `path` build another copy of the source into another library (the
+    mutation tests and the sanitizer build use them)."""
+    if src or path:
+        out = path or (_LIB + ".alt")
+        subprocess.check_call(["gcc"] + GCC_FLAGS + list(extra_flags) + [src or _SRC, "-o", out, "-lm"])
         return out
     if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
         tmp = _LIB + ".tmp%d" % os.getpid()

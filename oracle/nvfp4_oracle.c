@@ -47,14 +47,6 @@
 #include <math.h>
 #include <omp.h>
 
-/* Mutation testing: building with -DORACLE_MUTANT=k plants one deliberate,
- * plausible mistake (listed in tests/test_oracle_mutants.py) so the test
- * suite can show that its pins catch it.  The default build (0) has none. */
-#ifndef ORACLE_MUTANT
-#define ORACLE_MUTANT 0
-#endif
-#define MUT(k) (ORACLE_MUTANT == (k))
-
 /* number of OpenMP threads the parallel loops below use, and a way to set it
  * (the CPU baseline times the quantizer on one thread as well as on all) */
 int oracle_threads(void) { return omp_get_max_threads(); }
@@ -65,7 +57,7 @@ void oracle_set_threads(int n) { omp_set_num_threads(n > 0 ? n : 1); }
 /* E2M1 code (4 bits: sign, 2 exponent bits with bias 1, 1 mantissa bit) */
 double oracle_e2m1_value(int code) {
     int s = (code >> 3) & 1, e = (code >> 1) & 3, m = code & 1;
-    double mag = (e == 0) ? (MUT(17) ? 1.0 : 0.5) * m : (1.0 + 0.5 * m) * ldexp(1.0, e - 1);
+    double mag = (e == 0) ? 0.5 * m : (1.0 + 0.5 * m) * ldexp(1.0, e - 1);
     return s ? -mag : mag;
 }
 
@@ -74,7 +66,7 @@ double oracle_e2m1_value(int code) {
 double oracle_e4m3_value(int code) {
     int s = (code >> 7) & 1, e = (code >> 3) & 15, m = code & 7;
     if (e == 15 && m == 7) return NAN;
-    double mag = (e == 0) ? ldexp(m / 8.0, -6) : (1.0 + m / 8.0) * ldexp(1.0, e - (MUT(3) ? 8 : 7));
+    double mag = (e == 0) ? ldexp(m / 8.0, -6) : (1.0 + m / 8.0) * ldexp(1.0, e - 7);
     return s ? -mag : mag;
 }
 
@@ -94,7 +86,7 @@ static int rne_sat_search(double v, int ncodes, double (*value)(int)) {
         double t = value(c);
         if (isnan(t)) continue;
         double d = fabs(v - t);
-        if (best < 0 || d < bestd || (d == bestd && (MUT(2) || (c & 1) == 0))) { best = c; bestd = d; }
+        if (best < 0 || d < bestd || (d == bestd && (c & 1) == 0)) { best = c; bestd = d; }
     }
     return best;
 }
@@ -138,14 +130,14 @@ static void encode_row(const uint16_t* x, int64_t k, float S, uint8_t* q, uint8_
         if (S == 0.0f) {
             sc = 0;
         } else {
-            float t = (MUT(6) ? 4.0f : 6.0f) * S;
+            float t = 6.0f * S;
             float v = ab / t;
             sc = oracle_rne_sat_e4m3(v);
         }
         sb[b] = (uint8_t)sc;
         /* element codes */
         float sbv = (float)oracle_e4m3_value(sc);
-        float d = MUT(7) ? S : S * sbv;
+        float d = S * sbv;
         float inv = (d != 0.0f) ? 1.0f / d : 0.0f;
         uint8_t codes[16];
         for (int j = 0; j < 16; ++j) {
@@ -156,11 +148,10 @@ static void encode_row(const uint16_t* x, int64_t k, float S, uint8_t* q, uint8_
                 float r = xs[j] * inv;
                 mag = oracle_rne_sat_e2m1(fabsf(r));
             }
-            codes[j] = (uint8_t)((signbit(xs[j]) && !MUT(4) ? 8 : 0) | mag);
+            codes[j] = (uint8_t)((signbit(xs[j]) ? 8 : 0) | mag);
         }
         for (int j = 0; j < 8; ++j)
-            q[8 * b + j] = MUT(5) ? (uint8_t)(codes[2 * j + 1] | (codes[2 * j] << 4))
-                                  : (uint8_t)(codes[2 * j] | (codes[2 * j + 1] << 4));
+            q[8 * b + j] = (uint8_t)(codes[2 * j] | (codes[2 * j + 1] << 4));
     }
 }
 
@@ -185,8 +176,8 @@ int oracle_quantize_rows(const uint16_t* x, int64_t rows, int64_t k, const float
         const uint16_t* xr = x + r * k;
         for (int64_t j = 0; j < k; ++j)
             if (((xr[j] >> 7) & 0xFF) == 0xFF) bad = 1;
-        float amax = amax_in ? amax_in[r] : row_amax(xr, MUT(19) && k > 16 ? k - 16 : k);
-        float S = amax / (MUT(1) ? 2048.0f : 2688.0f);
+        float amax = amax_in ? amax_in[r] : row_amax(xr, k);
+        float S = amax / 2688.0f;
         s[r] = S;
         encode_row(xr, k, S, q + r * (k / 2), sb + r * (k / 16));
     }
@@ -214,7 +205,7 @@ int oracle_quantize_weight(const uint16_t* w, int64_t groups, int64_t rows_per_g
             }
         }
         if (amax_out) amax_out[g] = amax;
-        float S = amax / (MUT(1) ? 2048.0f : 2688.0f);
+        float S = amax / 2688.0f;
         s[g] = S;
         #pragma omp parallel for schedule(dynamic, 16) reduction(| : bad)
         for (int64_t r = 0; r < rows_per_group; ++r) {
@@ -263,7 +254,7 @@ static uint16_t f32_to_bf16_nearest(float v) {
     double dl = fabs((double)v - lv), dh = fabs(hv - (double)v);
     if (dl < dh) return lo;
     if (dh < dl) return hi;
-    return ((lo & 1) || MUT(16)) ? hi : lo;
+    return (lo & 1) ? hi : lo;
 }
 
 /* bf16 bit pattern nearest to a finite double x (ties to the even pattern;
@@ -324,9 +315,9 @@ int oracle_swiglu_rows(const float* gate_up, int64_t rows, int64_t f, uint16_t* 
     for (int64_t r = 0; r < rows; ++r) {
         const float* gr = gate_up + r * 2 * f;
         for (int64_t j = 0; j < f; ++j) {
-            double g = gr[MUT(13) ? f + j : j], u = gr[MUT(13) ? j : f + j];
+            double g = gr[j], u = gr[f + j];
             if (!isfinite(g) || !isfinite(u)) { bad = 1; h[r * f + j] = 0; continue; }
-            double hv = (g * u) / (1.0 + exp(MUT(12) ? g : -g));
+            double hv = (g * u) / (1.0 + exp(-g));
             float h32 = (float)hv;
             if (!isfinite(h32)) { bad = 1; h[r * f + j] = 0; continue; }
             h[r * f + j] = f32_to_bf16_nearest(h32);
@@ -366,7 +357,7 @@ int oracle_route(const float* logits, int64_t T, int64_t E, int64_t topk, int32_
                     if (experts[t * topk + i] == e) taken = 1;
                 if (taken) continue;
                 /* strictly greater wins, so among equal logits the lowest id stays */
-                if (best < 0 || (MUT(11) ? lt[e] >= lt[best] : lt[e] > lt[best])) best = e;
+                if (best < 0 || lt[e] > lt[best]) best = e;
             }
             experts[t * topk + j] = (int32_t)best;
         }
@@ -398,13 +389,12 @@ void oracle_dequantize_bf16(const uint8_t* q, const uint8_t* sb, const float* s,
                             int64_t rows, int64_t k, int64_t rows_per_scale, uint16_t* out) {
     #pragma omp parallel for schedule(static)
     for (int64_t r = 0; r < rows; ++r) {
-        double S = (double)s[MUT(20) ? r % rows_per_scale : r / rows_per_scale];
+        double S = (double)s[r / rows_per_scale];
         for (int64_t j = 0; j < k; ++j) {
             uint8_t byte = q[r * (k / 2) + j / 2];
             int code = (j & 1) ? (byte >> 4) : (byte & 15);
             double sbv = oracle_e4m3_value(sb[r * (k / 16) + j / 16]);
-            out[r * k + j] = MUT(14) ? f32_to_bf16_nearest((float)(S * sbv * oracle_e2m1_value(code)))
-                                     : f64_to_bf16_nearest(S * sbv * oracle_e2m1_value(code));
+            out[r * k + j] = f64_to_bf16_nearest(S * sbv * oracle_e2m1_value(code));
         }
     }
 }
@@ -424,7 +414,6 @@ static int mx_scale_exponent(double amax) {
     if (amax == 0.0) return -127;
     int e = -127;
     while (ldexp(448.0, e) < amax) ++e;   /* smallest e with amax <= 448 * 2^e */
-    if (MUT(15) && e > -127) e = (int)floor(log2(amax)) - 8;  /* rounded down */
     return e;
 }
 
@@ -449,7 +438,7 @@ int oracle_mxfp8_quantize_rows(const uint16_t* x, int64_t rows, int64_t k, uint8
                 /* |x| / 2^e is exact in double; the E4M3 search rounds it */
                 double v = ldexp(fabs((double)xv), -e);
                 int mag = rne_sat_search(v, 128, oracle_e4m3_value);
-                q[r * k + 32 * b + j] = (uint8_t)((signbit(xv) && !MUT(18) ? 0x80 : 0) | mag);
+                q[r * k + 32 * b + j] = (uint8_t)((signbit(xv) ? 0x80 : 0) | mag);
             }
         }
     }
@@ -515,7 +504,7 @@ static void dot_exact(const uint8_t* aq, const uint8_t* asb, const uint8_t* bq,
     int64_t acc = 0, aacc = 0;
     for (int64_t j = 0; j < k; ++j) {
         int ca = (j & 1) ? (aq[j / 2] >> 4) : (aq[j / 2] & 15);
-        int cb = ((j & 1) != MUT(9)) ? (bq[j / 2] >> 4) : (bq[j / 2] & 15);
+        int cb = (j & 1) ? (bq[j / 2] >> 4) : (bq[j / 2] & 15);
         int64_t ua = unit_int(asb[j / 16], ca);
         int64_t ub = unit_int(bsb[j / 16], cb);
         int64_t p = ua * ub;
@@ -539,7 +528,7 @@ void oracle_gemm_entries(const uint8_t* a_q, const uint8_t* a_sb, const float* a
         int64_t dot, absdot;
         dot_exact(a_q + a_row[i] * (k / 2), a_sb + a_row[i] * (k / 16),
                   b_q + b_row[i] * (k / 2), b_sb + b_row[i] * (k / 16), k, &dot, &absdot);
-        double sc = (double)a_s[a_row[i]] * (MUT(8) ? 1.0 : (double)b_s[b_scale[i]]) * 0x1.0p-20;
+        double sc = (double)a_s[a_row[i]] * (double)b_s[b_scale[i]] * 0x1.0p-20;
         y_ref[i] = sc * (double)dot;
         bound[i] = sc * (double)absdot;
     }
@@ -556,7 +545,7 @@ void oracle_gemm(const uint8_t* a_q, const uint8_t* a_sb, const float* a_s, int6
             int64_t dot, absdot;
             dot_exact(a_q + i * (k / 2), a_sb + i * (k / 16), b_q + j * (k / 2),
                       b_sb + j * (k / 16), k, &dot, &absdot);
-            double sc = (double)a_s[i] * (MUT(8) ? 1.0 : (double)b_s[0]) * 0x1.0p-20;
+            double sc = (double)a_s[i] * (double)b_s[0] * 0x1.0p-20;
             y_ref[i * n + j] = sc * (double)dot;
             bound[i * n + j] = sc * (double)absdot;
         }
@@ -576,12 +565,12 @@ void oracle_grouped_gemm(const uint8_t* a_q, const uint8_t* a_sb, const float* a
         int64_t lo = offsets[g], hi = offsets[g + 1];
         #pragma omp parallel for schedule(dynamic, 4)
         for (int64_t i = lo; i < hi; ++i) {
-            int64_t ar = (row_index && !MUT(10)) ? row_index[i] : i;
+            int64_t ar = row_index ? row_index[i] : i;
             for (int64_t j = 0; j < n; ++j) {
                 int64_t br = g * n + j, dot, absdot;
                 dot_exact(a_q + ar * (k / 2), a_sb + ar * (k / 16), b_q + br * (k / 2),
                           b_sb + br * (k / 16), k, &dot, &absdot);
-                double sc = (double)a_s[ar] * (MUT(8) ? 1.0 : (double)b_s[g]) * 0x1.0p-20;
+                double sc = (double)a_s[ar] * (double)b_s[g] * 0x1.0p-20;
                 y_ref[i * n + j] = sc * (double)dot;
                 bound[i * n + j] = sc * (double)absdot;
             }
