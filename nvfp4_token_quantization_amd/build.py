@@ -11,7 +11,7 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libnvfp4.so")
 SOURCES = ["abi_common.hip", "quantize.hip", "swiglu_quantize.hip", "route.hip", "dequantize.hip",
            "mxfp8.hip", "mxfp8_gemm.hip",
-           "gemm.hip"]
+           "gemm.hip", "gemm_skinny.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [
@@ -36,12 +36,13 @@ def _run(cmd):
     return r.returncode, _filter(r.stdout + r.stderr)
 
 
-def build(verbose=False, sources=None, lib=None, jobs=None):
+def build(verbose=False, sources=None, lib=None, jobs=None, extra_flags=()):
     """Compile `sources` (default: every source of the library) and link them
-    into `lib` (default: libnvfp4.so next to this file)."""
+    into `lib` (default: libnvfp4.so next to this file); `extra_flags` are
+    added to every compile."""
     sources = sources or SOURCES
     lib = lib or LIB
-    objdir = os.path.join(HERE, "_build")
+    objdir = os.path.join(os.path.dirname(os.path.abspath(lib)), "_build")
     os.makedirs(objdir, exist_ok=True)
     inc = ["-I", os.path.join(ROOT, "include"), "-I", CSRC]
     tag = "%d" % os.getpid()
@@ -49,7 +50,7 @@ def build(verbose=False, sources=None, lib=None, jobs=None):
 
     def compile_one(src):
         obj = os.path.join(objdir, os.path.splitext(src)[0] + "." + tag + ".o")
-        cmd = [HIPCC] + FLAGS + inc + ["-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [HIPCC] + FLAGS + list(extra_flags) + inc + ["-c", os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         rc, msg = _run(cmd)
@@ -57,10 +58,13 @@ def build(verbose=False, sources=None, lib=None, jobs=None):
 
     with ThreadPoolExecutor(max_workers=jobs) as ex:
         results = list(ex.map(compile_one, sources))
+    objs = [o for _, o, _, _ in results]
     failed = [(s, m) for s, _, rc, m in results if rc != 0]
     if failed:
+        for o in objs:
+            if os.path.exists(o):
+                os.remove(o)
         raise RuntimeError("hipcc failed:\n" + "\n".join("%s:\n%s" % f for f in failed))
-    objs = [o for _, o, _, _ in results]
     tmp = lib + ".tmp" + tag
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC"] + objs + ["-o", tmp]
     if verbose:

@@ -40,46 +40,11 @@
 // serves one region.  Grouped GEMMs derive the per-expert m-tile prefix from
 // the device offsets in every block, and ragged expert tiles run only their
 // non-empty 32-row slabs.
-#include "tile_sched.h"
+#include "gemm_common.h"
 
 namespace nvfp4 {
 
 constexpr int BK = 128;          // K elements per stage
-
-struct GemmArgs {
-  const uint8_t* a_q;
-  const uint8_t* a_sb;
-  const float* a_s;
-  int64_t a_rows;
-  const int32_t* row_index;  // grouped only (nullable)
-  const uint8_t* b_q;
-  const uint8_t* b_sb;
-  const float* b_s;
-  int64_t n, k;
-  float* y;
-  TileGrid t;  // output rows / expert offsets and the launch plan
-};
-
-__device__ __forceinline__ f16x2 as_h2(uint32_t v) { return __builtin_bit_cast(f16x2, v); }
-
-// 8 decoded fp16 units from one dword of codes and a (h, h) scale pair
-__device__ __forceinline__ f16x8 decode8(uint32_t w, f16x2 sc) {
-  f16x2 p0 = __builtin_bit_cast(f16x2, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 256.0f, 0));
-  f16x2 p1 = __builtin_bit_cast(f16x2, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 256.0f, 1));
-  f16x2 p2 = __builtin_bit_cast(f16x2, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 256.0f, 2));
-  f16x2 p3 = __builtin_bit_cast(f16x2, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 256.0f, 3));
-  p0 = p0 * sc;
-  p1 = p1 * sc;
-  p2 = p2 * sc;
-  p3 = p3 * sc;
-  return (f16x8){p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
-}
-
-// (code << 7, code << 7) as an fp16 pair: s_b * 2^-8 in both halves
-__device__ __forceinline__ f16x2 scale_pair(uint32_t scales4, int blk) {
-  uint32_t c = (scales4 >> (8 * blk)) & 0xFFu;
-  return as_h2((c << 7) | (c << 23));
-}
 
 // 8-byte load of bytes [off, off + 8) of a row with `valid` bytes (K tail):
 // bytes past `valid` read as zero and are never fetched.  `row + off` must be
@@ -99,9 +64,6 @@ __device__ __forceinline__ uint4 load16_codes(const uint8_t* row, int64_t off, i
   return make_uint4(lo.x, lo.y, hi.x, hi.y);
 }
 
-__device__ __forceinline__ uint32_t pick(const uint4& v, int t) {
-  return (t & 3) == 0 ? v.x : (t & 3) == 1 ? v.y : (t & 3) == 2 ? v.z : v.w;
-}
 
 // ---------------------------------------------------------------------------
 // Register-direct variant: one wave per block, block tile = wave tile =
@@ -251,11 +213,12 @@ __global__ __launch_bounds__(64) void gemm_rd_kernel(GemmArgs p) {
   const uint8_t* bq_base = p.b_q + (int64_t)g * p.n * (p.k / 2);
   const uint8_t* bsb_base = p.b_sb + (int64_t)g * p.n * (p.k / 16);
 
-  auto a_source = [&](int64_t out_row) -> int64_t {
-    if (out_row >= row_hi) return -1;
-    int64_t r = p.row_index ? (int64_t)p.row_index[out_row] : out_row;
-    return (r >= 0 && r < p.a_rows) ? r : -1;
-  };
+  // Source A rows of the tile's output rows: lane l looks up rows l and 64 + l
+  // (independent loads), other lanes' rows come by shuffle (TM <= 4).
+  static_assert(BM <= 128, "two rows per lane");
+  const int32_t src0 = (int32_t)gathered_row(p.row_index, p.a_rows, row_lo + lane, row_hi);
+  const int32_t src1 = BM > 64 ? (int32_t)gathered_row(p.row_index, p.a_rows, row_lo + 64 + lane, row_hi)
+                               : -1;
 
   const uint8_t* arow[TM];
   const uint8_t* asrow[TM];
@@ -263,7 +226,7 @@ __global__ __launch_bounds__(64) void gemm_rd_kernel(GemmArgs p) {
   const uint8_t* bsrow[TN];
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
-    const int64_t r = a_source(row_lo + 32 * i + li);
+    const int64_t r = __shfl(i >= 2 ? src1 : src0, (32 * i + li) & 63, 64);
     arow[i] = r >= 0 ? p.a_q + r * (p.k / 2) : nullptr;
     asrow[i] = r >= 0 ? p.a_sb + r * (p.k / 16) : nullptr;
   }
@@ -275,10 +238,8 @@ __global__ __launch_bounds__(64) void gemm_rd_kernel(GemmArgs p) {
   }
   {
     const float sbw = p.b_s[g];
-    for (int r = lane; r < BM; r += 64) {
-      const int64_t ar = a_source(row_lo + r);
-      s_rowscale[r] = (ar >= 0 ? p.a_s[ar] : 0.0f) * sbw;
-    }
+    if (lane < BM) s_rowscale[lane] = (src0 >= 0 ? p.a_s[src0] : 0.0f) * sbw;
+    if (BM > 64) s_rowscale[64 + lane] = (src1 >= 0 ? p.a_s[src1] : 0.0f) * sbw;
   }
 
   // K loop and epilogue over the valid 32-row slabs only (ragged expert
@@ -328,36 +289,12 @@ constexpr int LDS_SCALES_AT = 2 * LDS_CODES;
 constexpr int LDS_WAVE = 2 * LDS_CODES + 2 * LDS_SCALES;
 static_assert(LDS_WAVE * 4 <= 160 * 1024, "four waves per CU");
 
-typedef int i32x4 __attribute__((ext_vector_type(4)));
-
 __device__ __forceinline__ int lds_swz(int r) { return ((r >> 2) + (r & 2)) & 3; }
 
-// Raw buffer resource over `bytes` bytes at p (stride 0; loads whose VGPR
-// offset is at or past `bytes` read nothing).
-__device__ __forceinline__ i32x4 make_rsrc(const void* p, int64_t bytes) {
-  const uint64_t a = (uint64_t)p;
-  return (i32x4){(int)(uint32_t)a, (int)((a >> 32) & 0xFFFFu), (int)bytes, 0x00020000};
-}
-
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"
-// 16 bytes per lane from rsrc[voff + soff] to LDS[lds + 16 * lane] (the
-// operand rows, scale rows included, are 16-byte aligned: k % 256 == 0 and
-// 16-byte aligned base pointers)
-__device__ __forceinline__ void dma16(i32x4 rsrc, uint32_t voff, uint32_t soff, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %3\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
-               :: "v"(voff), "s"(rsrc), "s"(soff), "s"(lds) : "memory", "m0");
-}
-#pragma clang diagnostic pop
 // Streaming 4-byte store to rsrc[voff] (dropped when voff is out of range).
 __device__ __forceinline__ void store_nt(__amdgpu_buffer_rsrc_t rsrc, float v, uint32_t voff) {
   __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), rsrc, voff, 0, 2);
 }
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
-}
-__device__ __forceinline__ void wait_lgkmcnt0() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
 struct LdsOperands {
   i32x4 aq, as, bq, bs;
@@ -649,11 +586,11 @@ __global__ __launch_bounds__(64) void gemm_lds_kernel(GemmArgs p) {
   const int g = tr.g;
   const int64_t rowb = p.k / 2, rows_s = p.k / 16;
 
-  auto a_source = [&](int64_t out_row) -> int64_t {
-    if (out_row >= row_hi) return -1;
-    int64_t r = p.row_index ? (int64_t)p.row_index[out_row] : out_row;
-    return (r >= 0 && r < p.a_rows) ? r : -1;
-  };
+  // Source A rows of the tile's 128 output rows: lane l looks up rows l and
+  // 64 + l (two independent loads), every other lane's rows come by shuffle.
+  const int32_t src0 = (int32_t)gathered_row(p.row_index, p.a_rows, row_lo + lane, row_hi);
+  const int32_t src1 = (int32_t)gathered_row(p.row_index, p.a_rows, row_lo + 64 + lane, row_hi);
+  auto src_of = [&](int half, int l) -> int64_t { return __shfl(half ? src1 : src0, l, 64); };
 
   LdsOperands o;
   o.aq = make_rsrc(p.a_q, p.a_rows * rowb);
@@ -673,17 +610,17 @@ __global__ __launch_bounds__(64) void gemm_lds_kernel(GemmArgs p) {
     for (int u = 0; u < 2; ++u) {
       const int lr = 16 * u + cr;
       const uint32_t chunk = (uint32_t)((cc ^ lds_swz(lr)) * 16);
-      const int64_t r = a_source(row_lo + 32 * i + lr);
+      const int64_t r = src_of(i >= 2, (32 * i + lr) & 63);
       o.aoff[i][u] = r >= 0 ? (uint32_t)(r * rowb) + chunk : OOB;
       const int64_t c = n0 + 32 * i + lr;
       o.boff[i][u] = c < p.n ? (uint32_t)(c * rowb) + chunk : OOB;
     }
-    if (a_source(row_lo + 32 * i + li) >= 0) o.avalid |= 1u << i;
+    if (src_of(i >= 2, (32 * i + li) & 63) >= 0) o.avalid |= 1u << i;
     if (n0 + 32 * i + li < p.n) o.bvalid |= 1u << i;
   }
 #pragma unroll
   for (int q = 0; q < 2; ++q) {
-    const int64_t r = a_source(row_lo + 64 * q + lane);
+    const int64_t r = q ? src1 : src0;
     o.asoff[q] = r >= 0 ? (uint32_t)(r * rows_s) : OOB;
     const int64_t c = n0 + 64 * q + lane;
     o.bsoff[q] = c < p.n ? (uint32_t)(c * rows_s) : OOB;
@@ -691,9 +628,8 @@ __global__ __launch_bounds__(64) void gemm_lds_kernel(GemmArgs p) {
   // this lane's two epilogue row scales (rows lane and lane + 64), written to
   // LDS after the K loop
   const float sbw = p.b_s[g];
-  const int64_t ar0 = a_source(row_lo + lane), ar1 = a_source(row_lo + 64 + lane);
-  const float rs0 = (ar0 >= 0 ? p.a_s[ar0] : 0.0f) * sbw;
-  const float rs1 = (ar1 >= 0 ? p.a_s[ar1] : 0.0f) * sbw;
+  const float rs0 = (src0 >= 0 ? p.a_s[src0] : 0.0f) * sbw;
+  const float rs1 = (src1 >= 0 ? p.a_s[src1] : 0.0f) * sbw;
   const int vslabs = (int)min((int64_t)4, (row_hi - row_lo + 31) / 32);
   switch (vslabs) {
     case 4: lds_body<4>(p, o, s_lds, h, li, lane, row_lo, row_hi, n0, rs0, rs1); break;
@@ -757,7 +693,7 @@ extern "C" int nvfp4_gemm(const uint8_t* a_q, const uint8_t* a_sb, const float* 
   p.a_q = a_q; p.a_sb = a_sb; p.a_s = a_s; p.a_rows = m;
   p.row_index = nullptr; p.t.m_total = m; p.t.offsets = nullptr; p.t.groups = 1;
   p.b_q = b_q; p.b_sb = b_sb; p.b_s = b_s; p.n = n; p.k = k; p.y = y;
-  nvfp4::launch_gemm_rd<4, 4>(p, false, str);
+  if (!nvfp4::launch_gemm_skinny(p, false, str)) nvfp4::launch_gemm_rd<4, 4>(p, false, str);
   return nvfp4host::launch_status();
 }
 
@@ -789,6 +725,6 @@ extern "C" int nvfp4_grouped_gemm(const uint8_t* a_q, const uint8_t* a_sb, const
   p.b_q = b_q; p.b_sb = b_sb; p.b_s = b_s; p.n = n; p.k = k; p.y = y;
   // k == 0 needs no special case: the K loop is empty and the epilogue writes
   // zeros to exactly the rows the groups own
-  nvfp4::launch_gemm_rd<4, 4>(p, true, str);
+  if (!nvfp4::launch_gemm_skinny(p, true, str)) nvfp4::launch_gemm_rd<4, 4>(p, true, str);
   return nvfp4host::launch_status();
 }

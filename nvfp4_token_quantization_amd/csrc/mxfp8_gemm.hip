@@ -87,12 +87,7 @@ __global__ __launch_bounds__(256) void mxfp8_gemm_lds_kernel(MxGemmArgs p) {
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int r = (tid >> 3) + 32 * i;
-    const int64_t orow = row_lo + r;
-    int64_t src = -1;
-    if (orow < row_hi) {
-      src = p.row_index ? (int64_t)p.row_index[orow] : orow;
-      if (src < 0 || src >= p.a_rows) src = -1;
-    }
+    const int64_t src = gathered_row(p.row_index, p.a_rows, row_lo + r, row_hi);
     lrow_a[i] = src >= 0 ? (uint32_t)src : 0u;
     lmask_a |= (src >= 0 ? 1u : 0u) << i;
     lmask_b |= (n0 + r < p.n ? 1u : 0u) << i;
@@ -102,12 +97,7 @@ __global__ __launch_bounds__(256) void mxfp8_gemm_lds_kernel(MxGemmArgs p) {
   uint32_t smask_a = 0, smask_b = 0;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int64_t orow = row_lo + 128 * wm + 32 * i + li;
-    int64_t src = -1;
-    if (orow < row_hi) {
-      src = p.row_index ? (int64_t)p.row_index[orow] : orow;
-      if (src < 0 || src >= p.a_rows) src = -1;
-    }
+    const int64_t src = gathered_row(p.row_index, p.a_rows, row_lo + 128 * wm + 32 * i + li, row_hi);
     srow_a[i] = src >= 0 ? (uint32_t)src : 0u;
     smask_a |= (src >= 0 ? 1u : 0u) << i;
     smask_b |= (n0 + 128 * wn + 32 * i + li < p.n ? 1u : 0u) << i;

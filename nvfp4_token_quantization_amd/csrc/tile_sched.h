@@ -31,6 +31,92 @@ struct TileRange {
   int g;
 };
 
+// Per-expert m-tile prefix of a contiguous per-expert layout, from the
+// device offsets, by one wave of 64 lanes: s_prefix[g] = m-tiles of BM rows
+// of the experts before g (s_prefix[G] = the total), and each expert's
+// clamped row range [lo, hi) in the two arrays after the prefix (words
+// MAX_GROUPS + 1 and 2 (MAX_GROUPS + 1) on; RANGES false: the prefix alone,
+// MAX_GROUPS + 1 words).  Offsets are clamped to
+// [0, m_total] and made non-decreasing, so bad metadata cannot address rows
+// outside the output.  The caller synchronizes before reading s_prefix.
+template <int BM, bool RANGES = true>
+__device__ __forceinline__ void expert_tile_prefix(const int32_t* offsets, int G, int64_t m_total,
+                                                   int lane, int32_t* s_prefix) {
+  constexpr int GPT = MAX_GROUPS / 64;
+  uint32_t* s_lo = reinterpret_cast<uint32_t*>(s_prefix + (MAX_GROUPS + 1));
+  uint32_t* s_hi = reinterpret_cast<uint32_t*>(s_prefix + 2 * (MAX_GROUPS + 1));
+  // every load first (indices clamped to the G + 1 entries), so they are in
+  // flight together; a load under the per-entry condition below would wait
+  // for each one in turn
+  int32_t ov[GPT + 1];
+#pragma unroll
+  for (int i = 0; i <= GPT; ++i) ov[i] = offsets[min(lane * GPT + i, G)];
+  int32_t local = 0;
+  int32_t cnt[GPT];
+#pragma unroll
+  for (int i = 0; i < GPT; ++i) {
+    const int gg = lane * GPT + i;
+    int32_t c = 0;
+    if (gg < G) {
+      int64_t lo = min(max((int64_t)ov[i], (int64_t)0), m_total);
+      int64_t hi = min(max((int64_t)ov[i + 1], lo), m_total);
+      c = (int32_t)((hi - lo + BM - 1) / BM);
+      if (RANGES) {
+        s_lo[gg] = (uint32_t)lo;  // m_total <= 2^31
+        s_hi[gg] = (uint32_t)hi;
+      }
+    }
+    cnt[i] = c;
+    local += c;
+  }
+  int32_t incl = local;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    int32_t o = __shfl_up(incl, d, 64);
+    if (lane >= d) incl += o;
+  }
+  int32_t run = incl - local;
+#pragma unroll
+  for (int i = 0; i < GPT; ++i) {
+    const int gg = lane * GPT + i;
+    if (gg <= G) s_prefix[gg] = run;
+    run += cnt[i];
+  }
+  // the loop covers entries 0..MAX_GROUPS - 1; with G == MAX_GROUPS the
+  // total (entry G) is the last lane's final running sum
+  if (G == MAX_GROUPS && lane == 63) s_prefix[MAX_GROUPS] = run;
+}
+
+// The expert that owns global m-tile mt (mt < s_prefix[G]): the last g with
+// s_prefix[g] <= mt, so experts without tiles are skipped.
+__device__ __forceinline__ int find_expert(const int32_t* s_prefix, int G, int64_t mt) {
+  int lo = 0, hi = G - 1;
+  while (lo < hi) {
+    int mid = (lo + hi + 1) >> 1;
+    if (s_prefix[mid] <= mt) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+// A readable int32 for the gathered-row load below when there is no index
+// (its value is never used).
+__device__ int32_t k_no_row_index[1] = {0};
+
+// The A row that output row `out_row` of a tile with rows [.., row_hi)
+// reads: row_index[out_row] (or out_row itself without an index), -1 when
+// the output row is past the tile or the index falls outside [0, a_rows).
+// The index load is unconditional and branch-free (clamped to the tile's
+// last row, which exists; a dummy word without an index), so the loads of a
+// lane's rows go out together instead of each waiting behind a branch.
+__device__ __forceinline__ int64_t gathered_row(const int32_t* row_index, int64_t a_rows,
+                                                int64_t out_row, int64_t row_hi) {
+  const int64_t rr = min(out_row, row_hi - 1);
+  const int32_t* src = row_index ? row_index + rr : k_no_row_index;
+  const int32_t v = *src;
+  const int64_t r = row_index ? (int64_t)v : rr;
+  return (out_row < row_hi && r >= 0 && r < a_rows) ? r : -1;
+}
+
 // Blocks are dealt round-robin to the 8 XCDs (block b runs on XCD b % 8);
 // each XCD owns one region of an (8 / xcd_n) x xcd_n split of the tile grid
 // so its L2 holds that region's A rows and B columns.  Inside a region, n runs
@@ -42,7 +128,6 @@ template <int BM, int BN>
 __device__ __forceinline__ bool schedule_tile(const TileGrid& t, int lane,
                                               int32_t* s_prefix /* SCHED_LDS_WORDS */,
                                               TileRange& out) {
-  constexpr int GPT = MAX_GROUPS / 64;
   const int xcd = blockIdx.x % 8;
   const int64_t jloc = blockIdx.x / 8;
   const int xn = xcd % t.xcd_n, xm = xcd / t.xcd_n, XM = 8 / t.xcd_n;
@@ -75,40 +160,9 @@ __device__ __forceinline__ bool schedule_tile(const TileGrid& t, int lane,
   int g = 0;
   if (t.offsets) {
     const int G = t.groups;
-    uint32_t* s_lo = reinterpret_cast<uint32_t*>(s_prefix + (MAX_GROUPS + 1));
-    uint32_t* s_hi = reinterpret_cast<uint32_t*>(s_prefix + 2 * (MAX_GROUPS + 1));
-    int32_t local = 0;
-    int32_t cnt[GPT];
-#pragma unroll
-    for (int i = 0; i < GPT; ++i) {
-      const int gg = lane * GPT + i;
-      int32_t c = 0;
-      if (gg < G) {
-        int64_t lo = min(max((int64_t)t.offsets[gg], (int64_t)0), t.m_total);
-        int64_t hi = min(max((int64_t)t.offsets[gg + 1], lo), t.m_total);
-        c = (int32_t)((hi - lo + BM - 1) / BM);
-        s_lo[gg] = (uint32_t)lo;  // m_total <= 2^31
-        s_hi[gg] = (uint32_t)hi;
-      }
-      cnt[i] = c;
-      local += c;
-    }
-    int32_t incl = local;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-      int32_t o = __shfl_up(incl, d, 64);
-      if (lane >= d) incl += o;
-    }
-    int32_t run = incl - local;
-#pragma unroll
-    for (int i = 0; i < GPT; ++i) {
-      const int gg = lane * GPT + i;
-      if (gg <= G) s_prefix[gg] = run;
-      run += cnt[i];
-    }
-    // the loop covers entries 0..MAX_GROUPS - 1; with G == MAX_GROUPS the
-    // total (entry G) is the last lane's final running sum
-    if (G == MAX_GROUPS && lane == 63) s_prefix[MAX_GROUPS] = run;
+    const uint32_t* s_lo = reinterpret_cast<const uint32_t*>(s_prefix + (MAX_GROUPS + 1));
+    const uint32_t* s_hi = reinterpret_cast<const uint32_t*>(s_prefix + 2 * (MAX_GROUPS + 1));
+    expert_tile_prefix<BM>(t.offsets, G, t.m_total, lane, s_prefix);
     __syncthreads();
     const int64_t total_mt = s_prefix[G];
     const int64_t mpx = (total_mt + XM - 1) / XM;
@@ -116,12 +170,7 @@ __device__ __forceinline__ bool schedule_tile(const TileGrid& t, int lane,
     if (!place(mcount, jf, hf)) return false;  // block-uniform
     mt = xm * mpx + jf / width;
     nt = nlo + jf % width;
-    int lo = 0, hi = G - 1;
-    while (lo < hi) {
-      int mid = (lo + hi + 1) >> 1;
-      if (s_prefix[mid] <= mt) lo = mid; else hi = mid - 1;
-    }
-    g = lo;
+    g = find_expert(s_prefix, G, mt);
     const int64_t glo = (int64_t)s_lo[g];
     const int64_t ghi = (int64_t)s_hi[g];
     row_lo = glo + (mt - s_prefix[g]) * BM;
