@@ -13,7 +13,9 @@ Functions keep the C names:
   nvfp4_quantize_weight(w, amax_in=None)          -> (q, sb, s, amax)
   nvfp4_gemm(a, b)                                -> y
   nvfp4_grouped_gemm(a, offsets, b, row_index=None, m_total=None) -> y
-  nvfp4_debug_encode_e2m1(v), nvfp4_debug_encode_e4m3(v)   (codec hooks)
+
+(The codec self-test hooks live in the test-only ``selftest`` submodule over
+``libnvfp4_selftest.so``.)
 
 Layouts (all row-major): x bf16 [rows, k]; q uint8 [rows, k/2] with element
 2i in the low nibble; sb uint8 [rows, k/16] (E4M3 codes); s float32 [rows]
@@ -60,16 +62,10 @@ def lib():
         L.nvfp4_mxfp8_quantize_rows.argtypes = [P, I64, I64, P, P, P]
         L.nvfp4_mxfp8_gemm.argtypes = [P, P, I64, P, P, I64, I64, P, P]
         L.nvfp4_mxfp8_grouped_gemm.argtypes = [P, P, I64, P, I64, P, I64, P, P, I64, I64, P, P]
-        L.nvfp4_debug_encode_fp8.argtypes = [P, I64, P, P]
-        L.nvfp4_debug_encode_e2m1.argtypes = [P, I64, P, P]
-        L.nvfp4_debug_encode_e4m3.argtypes = [P, I64, P, P]
-        L.nvfp4_debug_block_scale.argtypes = [P, P, I64, P, P, P]
         for f in ("nvfp4_quantize_rows", "nvfp4_quantize_weight", "nvfp4_gemm",
                   "nvfp4_swiglu_quantize_rows", "nvfp4_moe_route", "nvfp4_dequantize_rows",
-                  "nvfp4_mxfp8_quantize_rows", "nvfp4_debug_encode_fp8", "nvfp4_mxfp8_gemm",
-                  "nvfp4_mxfp8_grouped_gemm",
-                  "nvfp4_grouped_gemm", "nvfp4_debug_encode_e2m1", "nvfp4_debug_encode_e4m3",
-                  "nvfp4_debug_block_scale"):
+                  "nvfp4_mxfp8_quantize_rows", "nvfp4_mxfp8_gemm", "nvfp4_mxfp8_grouped_gemm",
+                  "nvfp4_grouped_gemm"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -442,47 +438,3 @@ def nvfp4_grouped_gemm(a, offsets, b, row_index=None, m_total=None, out=None):
                                   n, k, _ptr(y), _stream(dev))
     _check("nvfp4_grouped_gemm", st)
     return y
-
-
-def nvfp4_debug_encode_e2m1(v):
-    """Device E2M1 code (sign | RNE_SAT magnitude) of each float32 in v."""
-    _dev(v, "v", (torch.float32,))
-    out = torch.empty(v.shape, dtype=torch.uint8, device=v.device)
-    _check("nvfp4_debug_encode_e2m1",
-           lib().nvfp4_debug_encode_e2m1(_ptr(v), v.numel(), _ptr(out), _stream(v.device)))
-    return out
-
-
-def nvfp4_debug_encode_e4m3(v):
-    """Device RNE_SAT E4M3 code of each non-negative float32 in v."""
-    _dev(v, "v", (torch.float32,))
-    out = torch.empty(v.shape, dtype=torch.uint8, device=v.device)
-    _check("nvfp4_debug_encode_e4m3",
-           lib().nvfp4_debug_encode_e4m3(_ptr(v), v.numel(), _ptr(out), _stream(v.device)))
-    return out
-
-
-def nvfp4_debug_block_scale(block_amax, amax):
-    """The quantizer's block-scale step on arbitrary inputs: block_amax int16
-    (bf16 bits of a block's largest magnitude) and amax float32 (the row's
-    amax), same shape.  Returns (code uint8, inv float32)."""
-    _dev(block_amax, "block_amax", (torch.int16,))
-    _dev(amax, "amax", (torch.float32,))
-    if block_amax.shape != amax.shape:
-        raise ValueError("block_amax and amax differ in shape")
-    code = torch.empty(amax.shape, dtype=torch.uint8, device=amax.device)
-    inv = torch.empty(amax.shape, dtype=torch.float32, device=amax.device)
-    _check("nvfp4_debug_block_scale",
-           lib().nvfp4_debug_block_scale(_ptr(block_amax), _ptr(amax), amax.numel(), _ptr(code),
-                                         _ptr(inv), _stream(amax.device)))
-    return code, inv
-
-
-def nvfp4_debug_encode_fp8(v):
-    """E4M3 code (sign | RNE_SAT magnitude) of each float32 in v through the
-    pack-convert the MXFP8 quantizer uses (specified for |v| <= 448)."""
-    _dev(v, "v", (torch.float32,))
-    out = torch.empty(v.shape, dtype=torch.uint8, device=v.device)
-    _check("nvfp4_debug_encode_fp8",
-           lib().nvfp4_debug_encode_fp8(_ptr(v), v.numel(), _ptr(out), _stream(v.device)))
-    return out

@@ -1,5 +1,6 @@
-"""Build libnvfp4.so (HIP, gfx950) in-tree with hipcc: one object per source,
-compiled in parallel, then linked into the shared library."""
+"""Build libnvfp4.so (HIP, gfx950) and the test-only codec self-test library
+libnvfp4_selftest.so in-tree with hipcc: one object per source, compiled in
+parallel, then linked into the shared libraries."""
 import os
 import subprocess
 import sys
@@ -9,9 +10,10 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libnvfp4.so")
-SOURCES = ["abi_common.hip", "quantize.hip", "swiglu_quantize.hip", "route.hip", "dequantize.hip",
-           "mxfp8.hip", "mxfp8_gemm.hip",
-           "gemm.hip", "gemm_skinny.hip"]
+SOURCES = ["abi_common.hip", "host_util.hip", "quantize.hip", "swiglu_quantize.hip", "route.hip",
+           "dequantize.hip", "mxfp8.hip", "mxfp8_gemm.hip", "gemm.hip", "gemm_skinny.hip"]
+SELFTEST_LIB = os.path.join(HERE, "libnvfp4_selftest.so")
+SELFTEST_SOURCES = ["selftest.hip", "host_util.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [
@@ -37,16 +39,20 @@ def _run(cmd):
 
 
 def build(verbose=False, sources=None, lib=None, jobs=None, extra_flags=()):
-    """Compile `sources` (default: every source of the library) and link them
-    into `lib` (default: libnvfp4.so next to this file); `extra_flags` are
-    added to every compile."""
-    sources = sources or SOURCES
-    lib = lib or LIB
-    objdir = os.path.join(os.path.dirname(os.path.abspath(lib)), "_build")
+    """Compile and link the libraries.  By default: libnvfp4.so from SOURCES
+    and libnvfp4_selftest.so from SELFTEST_SOURCES (each source compiled
+    once).  With `sources` and `lib`: that one library.  `extra_flags` are
+    added to every compile.  Returns the path of the (first) library."""
+    if sources or lib:
+        targets = [(lib or LIB, list(sources or SOURCES))]
+    else:
+        targets = [(LIB, SOURCES), (SELFTEST_LIB, SELFTEST_SOURCES)]
+    allsrc = sorted({s for _, srcs in targets for s in srcs})
+    objdir = os.path.join(os.path.dirname(os.path.abspath(targets[0][0])), "_build")
     os.makedirs(objdir, exist_ok=True)
     inc = ["-I", os.path.join(ROOT, "include"), "-I", CSRC]
     tag = "%d" % os.getpid()
-    jobs = jobs or min(len(sources), int(os.environ.get("MAX_JOBS", "8")), os.cpu_count() or 1)
+    jobs = jobs or min(len(allsrc), int(os.environ.get("MAX_JOBS", "8")), os.cpu_count() or 1)
 
     def compile_one(src):
         obj = os.path.join(objdir, os.path.splitext(src)[0] + "." + tag + ".o")
@@ -57,25 +63,27 @@ def build(verbose=False, sources=None, lib=None, jobs=None, extra_flags=()):
         return src, obj, rc, msg
 
     with ThreadPoolExecutor(max_workers=jobs) as ex:
-        results = list(ex.map(compile_one, sources))
-    objs = [o for _, o, _, _ in results]
+        results = list(ex.map(compile_one, allsrc))
+    obj_of = {s: o for s, o, _, _ in results}
     failed = [(s, m) for s, _, rc, m in results if rc != 0]
-    if failed:
-        for o in objs:
+    try:
+        if failed:
+            raise RuntimeError("hipcc failed:\n" + "\n".join("%s:\n%s" % f for f in failed))
+        for path, srcs in targets:
+            tmp = path + ".tmp" + tag
+            cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC"] + [obj_of[s] for s in srcs]
+            cmd += ["-o", tmp]
+            if verbose:
+                print(" ".join(cmd), flush=True)
+            rc, msg = _run(cmd)
+            if rc != 0:
+                raise RuntimeError("link failed:\n" + msg)
+            os.replace(tmp, path)
+    finally:
+        for o in obj_of.values():
             if os.path.exists(o):
                 os.remove(o)
-        raise RuntimeError("hipcc failed:\n" + "\n".join("%s:\n%s" % f for f in failed))
-    tmp = lib + ".tmp" + tag
-    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC"] + objs + ["-o", tmp]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    rc, msg = _run(cmd)
-    for o in objs:
-        os.remove(o)
-    if rc != 0:
-        raise RuntimeError("link failed:\n" + msg)
-    os.replace(tmp, lib)
-    return lib
+    return targets[0][0]
 
 
 if __name__ == "__main__":

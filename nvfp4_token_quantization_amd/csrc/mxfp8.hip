@@ -17,33 +17,9 @@
 // of lanes: two DPP steps give all four lanes the block amax and its scale,
 // each lane converts its 8 elements into 8 bytes (non-temporal stores: the
 // codes are not read again here) and the quad's first lane stores the scale.
-#include "nvfp4_internal.h"
+#include "mxfp8_codec.h"
 
 namespace nvfp4 {
-
-typedef short s16x2 __attribute__((ext_vector_type(2)));
-
-// E8M0 scale code for a block whose largest magnitude has bf16 bits `a`
-__device__ __forceinline__ uint32_t mx_scale_code(uint32_t a) {
-  const int ef = (int)(a >> 7);  // biased exponent field (sign already cleared)
-  if (ef == 0) return 0u;        // zero or subnormal amax: smallest scale
-  const int code = ef - 8 + ((a & 0x7Fu) > 96u ? 1 : 0);
-  return (uint32_t)(code < 0 ? 0 : (code > 254 ? 254 : code));
-}
-
-// two fp32 values -> two E4M3 codes in the low (SEL = 0) or high 16 bits
-template <bool HI>
-__device__ __forceinline__ uint32_t fp8_encode2(uint32_t old, float a, float b) {
-  s16x2 o = __builtin_bit_cast(s16x2, old);
-  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(o, a, b, 1.0f, HI));
-}
-
-__device__ __forceinline__ uint32_t fp8_encode4(uint32_t w0, uint32_t w1, float inv) {
-  uint32_t r = fp8_encode2<false>(0u, __uint_as_float(w0 << 16) * inv,
-                                  __uint_as_float(w0 & 0xFFFF0000u) * inv);
-  return fp8_encode2<true>(r, __uint_as_float(w1 << 16) * inv,
-                           __uint_as_float(w1 & 0xFFFF0000u) * inv);
-}
 
 template <typename IDX, int U>
 __global__ __launch_bounds__(256) void mxfp8_quantize_kernel(const uint16_t* __restrict__ x,
@@ -81,12 +57,6 @@ __global__ __launch_bounds__(256) void mxfp8_quantize_kernel(const uint16_t* __r
   }
 }
 
-__global__ __launch_bounds__(256) void debug_fp8_kernel(const float* __restrict__ v, int64_t n,
-                                                        uint8_t* __restrict__ code) {
-  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
-    code[i] = (uint8_t)(fp8_encode2<false>(0u, v[i], 0.0f) & 0xFFu);
-}
-
 }  // namespace nvfp4
 
 using nvfp4host::aligned;
@@ -113,18 +83,5 @@ extern "C" int nvfp4_mxfp8_quantize_rows(const uint16_t* x_bf16, int64_t rows, i
   else
     hipLaunchKernelGGL((nvfp4::mxfp8_quantize_kernel<uint64_t, U>), grid, dim3(256), 0, str, x_bf16,
                        (uint64_t)nchunks, q, sc);
-  return nvfp4host::launch_status();
-}
-
-extern "C" int nvfp4_debug_encode_fp8(const float* v, int64_t n, uint8_t* code, void* stream) {
-  if (n < 0) return NVFP4_ERROR_INVALID_VALUE;
-  if (n == 0) return NVFP4_SUCCESS;
-  if (!v || !code) return NVFP4_ERROR_INVALID_VALUE;
-  if (!aligned(v, 4)) return NVFP4_ERROR_MISALIGNED;
-  int st = nvfp4host::check_arch();
-  if (st) return st;
-  const int64_t need = (n + 255) / 256;
-  dim3 grid((unsigned)(need < 4096 ? need : 4096));
-  hipLaunchKernelGGL(nvfp4::debug_fp8_kernel, grid, dim3(256), 0, (hipStream_t)stream, v, n, code);
   return nvfp4host::launch_status();
 }

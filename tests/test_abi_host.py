@@ -1,6 +1,8 @@
 """Host-side checks of the C ABI (no GPU needed).
 
-- libnvfp4.so loads and exports every function include/nvfp4.h declares;
+- libnvfp4.so loads and exports every function include/nvfp4.h declares and
+  no self-test hook; libnvfp4_selftest.so exports those include/
+  nvfp4_selftest.h declares;
 - argument errors return the documented status before any HIP call
   (null pointers, negative sizes, k % 16 != 0, misaligned pointers, zero
   groups), and empty problems return success without launching.
@@ -13,6 +15,7 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "nvfp4.h")
+SELFTEST_HEADER = os.path.join(ROOT, "include", "nvfp4_selftest.h")
 
 OK, INVALID, SHAPE, MISALIGNED = 0, 1, 2, 3
 
@@ -23,8 +26,14 @@ def L():
     return nv.lib()
 
 
-def declared_functions():
-    txt = open(HEADER).read()
+@pytest.fixture(scope="module")
+def S():
+    import nvfp4_token_quantization_amd.selftest as st
+    return st.lib()
+
+
+def declared_functions(header=HEADER):
+    txt = open(header).read()
     return re.findall(r"^(?:int|const char\*)\s+(nvfp4_\w+)\(", txt, re.M)
 
 
@@ -38,6 +47,16 @@ def test_header_declares_the_boundary():
 def test_library_exports_every_declared_symbol(L):
     for name in declared_functions():
         assert hasattr(L, name), name
+
+
+def test_selftest_hooks_live_outside_the_product_library(L, S):
+    hooks = declared_functions(SELFTEST_HEADER)
+    assert sorted(hooks) == ["nvfp4_debug_block_scale", "nvfp4_debug_encode_e2m1",
+                             "nvfp4_debug_encode_e4m3", "nvfp4_debug_encode_fp8"]
+    assert not set(hooks) & set(declared_functions())
+    for name in hooks:
+        assert hasattr(S, name), name
+        assert not hasattr(L, name), name
 
 
 def test_status_strings_and_version(L):
@@ -149,11 +168,13 @@ def test_dequantize_argument_errors(L):
     assert f(None, None, None, 0, 16, 1, None, None) == OK
 
 
-def test_debug_hooks_argument_errors(L):
-    assert L.nvfp4_debug_encode_e2m1(None, 4, P(FAKE), None) == INVALID
-    assert L.nvfp4_debug_encode_e4m3(P(FAKE), -1, P(FAKE), None) == INVALID
-    assert L.nvfp4_debug_encode_e4m3(P(FAKE + 1), 4, P(FAKE), None) == MISALIGNED
-    assert L.nvfp4_debug_encode_e2m1(None, 0, None, None) == OK
+def test_debug_hooks_argument_errors(S):
+    assert S.nvfp4_debug_encode_e2m1(None, 4, P(FAKE), None) == INVALID
+    assert S.nvfp4_debug_encode_e4m3(P(FAKE), -1, P(FAKE), None) == INVALID
+    assert S.nvfp4_debug_encode_e4m3(P(FAKE + 1), 4, P(FAKE), None) == MISALIGNED
+    assert S.nvfp4_debug_encode_e2m1(None, 0, None, None) == OK
+    assert S.nvfp4_debug_encode_fp8(None, 4, P(FAKE), None) == INVALID
+    assert S.nvfp4_debug_block_scale(P(FAKE), P(FAKE), 4, None, P(FAKE), None) == INVALID
 
 
 def test_binding_fails_loudly_without_gpu_tensors():

@@ -6,6 +6,7 @@ import pytest
 import torch
 
 import nvfp4_token_quantization_amd as nv
+import nvfp4_token_quantization_amd.selftest as st
 import oracle
 import synthgen as sg
 from gpu_helpers import dev, to_dev, to_np, workload
@@ -32,13 +33,13 @@ def test_fp8_convert_exhaustive():
     sides of every rounding boundary; negative inputs give the sign bit."""
     END = 0x43E00001  # through 448.0
     last = -1
-    for a, codes in _sweep(nv.nvfp4_debug_encode_fp8, 0, END):
+    for a, codes in _sweep(st.nvfp4_debug_encode_fp8, 0, END):
         c = codes.to(torch.int16)
         assert int(c.max()) <= 0x7E
         assert bool(torch.all(c[1:] >= c[:-1])), "not monotone in chunk at %#x" % a
         assert int(c[0]) >= last
         last = int(c[-1])
-        neg = nv.nvfp4_debug_encode_fp8(
+        neg = st.nvfp4_debug_encode_fp8(
             (torch.arange(a, a + c.numel(), dtype=torch.int64, device=dev()) | 0x80000000)
             .to(torch.int32).view(torch.float32))
         assert bool(torch.all(neg.to(torch.int16) == (c | 0x80))), "sign handling at %#x" % a
@@ -49,7 +50,7 @@ def test_fp8_convert_exhaustive():
         pts += [f, np.nextafter(f, np.float32(0)), np.nextafter(f, np.float32(np.inf))]
     pts += list(tab.astype(np.float32))
     v = np.array(pts, np.float32)
-    got = to_np(nv.nvfp4_debug_encode_fp8(to_dev(v)))
+    got = to_np(st.nvfp4_debug_encode_fp8(to_dev(v)))
     assert np.array_equal(got, oracle.rne_sat_e4m3(v))
 
 

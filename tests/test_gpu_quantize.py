@@ -12,6 +12,7 @@ import pytest
 import torch
 
 import nvfp4_token_quantization_amd as nv
+import nvfp4_token_quantization_amd.selftest as st
 import oracle
 import synthgen as sg
 from gpu_helpers import assert_same_quant, dev, oracle_rows, oracle_weight, to_dev, to_np, workload
@@ -235,13 +236,13 @@ def test_e2m1_codec_exhaustive():
     value); negative inputs must give the positive code with the sign bit."""
     POS_END = 0x7F800001   # through +inf
     last = -1
-    for a, codes in _sweep(nv.nvfp4_debug_encode_e2m1, 0, POS_END):
+    for a, codes in _sweep(st.nvfp4_debug_encode_e2m1, 0, POS_END):
         c = codes.to(torch.int16)
         assert int(c.max()) <= 7
         assert bool(torch.all(c[1:] >= c[:-1])), "not monotone in chunk at %#x" % a
         assert int(c[0]) >= last
         last = int(c[-1])
-        neg = nv.nvfp4_debug_encode_e2m1(
+        neg = st.nvfp4_debug_encode_e2m1(
             (torch.arange(a, a + c.numel(), dtype=torch.int64, device=dev()) | 0x80000000)
             .to(torch.int32).view(torch.float32))
         assert bool(torch.all(neg.to(torch.int16) == (c | 8))), "sign handling at %#x" % a
@@ -253,7 +254,7 @@ def test_e2m1_codec_exhaustive():
         pts += [f, np.nextafter(f, np.float32(0)), np.nextafter(f, np.float32(np.inf))]
     pts += list(grid.astype(np.float32))
     v = np.array(pts, np.float32)
-    got = to_np(nv.nvfp4_debug_encode_e2m1(to_dev(v)))
+    got = to_np(st.nvfp4_debug_encode_e2m1(to_dev(v)))
     assert np.array_equal(got, oracle.rne_sat_e2m1(v)), list(zip(v, got, oracle.rne_sat_e2m1(v)))
 
 
@@ -262,7 +263,7 @@ def test_e4m3_codec_exhaustive():
     E4M3 block-scale rounding: non-decreasing, and equal to the oracle on both
     sides of all 126 boundaries, at every code value, at 0 and at +inf."""
     last = -1
-    for a, codes in _sweep(nv.nvfp4_debug_encode_e4m3, 0, 0x7F800001):
+    for a, codes in _sweep(st.nvfp4_debug_encode_e4m3, 0, 0x7F800001):
         c = codes.to(torch.int16)
         assert int(c.max()) <= 0x7E
         assert bool(torch.all(c[1:] >= c[:-1])), "not monotone in chunk at %#x" % a
@@ -277,7 +278,7 @@ def test_e4m3_codec_exhaustive():
     pts += [np.float32(448.0), np.nextafter(np.float32(448.0), np.float32(np.inf)), np.float32(464.0),
             np.float32(480.0)]
     v = np.array(pts, np.float32)
-    got = to_np(nv.nvfp4_debug_encode_e4m3(to_dev(v)))
+    got = to_np(st.nvfp4_debug_encode_e4m3(to_dev(v)))
     assert np.array_equal(got, oracle.rne_sat_e4m3(v))
 
 
@@ -305,7 +306,7 @@ def _block_scale_expected(bbits, amax):
 
 
 def _check_block_scale(bbits, amax, what):
-    code, inv = nv.nvfp4_debug_block_scale(to_dev(bbits.view(np.int16)), to_dev(amax))
+    code, inv = st.nvfp4_debug_block_scale(to_dev(bbits.view(np.int16)), to_dev(amax))
     code, inv = to_np(code), to_np(inv)
     want_code, want_inv = _block_scale_expected(bbits, amax)
     bad = np.flatnonzero((code != want_code) | (inv.view(np.uint32) != want_inv.view(np.uint32)))
