@@ -42,7 +42,6 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, GB/s
 MFMA_F16_PEAK_TFS = 2500.0   # MI355X dense fp16/bf16 MFMA, TFLOP/s
-MFMA_FP8_PEAK_TFS = 5000.0   # MI355X dense fp8 MFMA, TFLOP/s
 
 
 def log(*a):
@@ -409,7 +408,7 @@ def main():
             ts.append(a.elapsed_time(b) / len(fns))
         return float(np.median(ts))
 
-    rot = {}
+    rot, rot_ms = {}, {}
     if not args.no_next:
         for name, src, amax, rows, kk in (("quantize_rows_dense", X2[0], None, M2, K2),
                                          ("quantize_rows_moe", X3[0], None, T3, K3),
@@ -423,11 +422,23 @@ def main():
                 p(x), rows, kk, None if am is None else p(am), p(q), p(sb), p(sc), sp))
                 for x, am, q, sb, sc in sets]
             ms = time_rotated(fns)
+            rot_ms[name] = ms
             ach = work[name][1] / (ms * 1e-3) / 1e9
             rot[name] = {"ms": round(ms, 4), "GB/s": round(ach, 1), "frac_hbm": round(ach / HBM_PEAK_GBS, 4),
                          "bytes": int(work[name][1]), "input_sets": R}
             del sets, fns
             torch.cuda.empty_cache()
+        # time = fixed + bytes / rate over the three shapes (least squares):
+        # the fixed part is the per-launch cost (launch, ramp-up, drain) and
+        # the rate the streaming rate once a launch is under way
+        xs = np.array([rot[nm]["bytes"] for nm in rot_ms], float)
+        ys = np.array([rot_ms[nm] * 1e3 for nm in rot_ms], float)
+        slope, icpt = np.polyfit(xs, ys, 1)
+        marginal = 1e-3 / slope  # GB/s (bytes per us -> GB/s)
+        rot["fit"] = {"fixed_us_per_launch": round(float(icpt), 2),
+                      "marginal_GB/s": round(float(marginal), 1),
+                      "marginal_frac_hbm": round(float(marginal) / HBM_PEAK_GBS, 4),
+                      "fixed_share": {nm: round(float(icpt) / (rot_ms[nm] * 1e3), 3) for nm in rot_ms}}
         log("quantizers, rotated inputs: %s" % rot)
 
     # Rollout-decode skinny shapes (64 tokens): dense 64 x 2560 -> 9728 and
@@ -527,7 +538,7 @@ def main():
                          "frac_hbm": round(byt / ms / 1e6 / HBM_PEAK_GBS, 4), "bytes": int(byt)}
             del dq
         # MXFP8 variant: quantize the dense activation, then the dense and the
-        # grouped up-projection GEMMs on the scaled fp8 MFMA
+        # grouped up-projection GEMMs (exact decode to bf16, bf16 MFMA)
         mx_x2 = (empty((M2, K2), u8), empty((M2, K2 // 32), u8))
         mx_w2 = (empty((N2, K2), u8), empty((N2, K2 // 32), u8))
         mx_x3 = (empty((T3, K3), u8), empty((T3, K3 // 32), u8))
@@ -544,13 +555,13 @@ def main():
                                                    N2, K2, p(out["y2"]), sp), K)
         fl = 2.0 * M2 * N2 * K2
         nxt["mxfp8_gemm_dense"] = {"ms": round(ms, 4), "TFLOP/s": round(fl / ms / 1e9, 1),
-                                   "frac_mfma_fp8": round(fl / ms / 1e9 / MFMA_FP8_PEAK_TFS, 4), "flop": fl}
+                                   "frac_mfma_bf16": round(fl / ms / 1e9 / MFMA_F16_PEAK_TFS, 4), "flop": fl}
         ms = time_extra(lambda: L.nvfp4_mxfp8_grouped_gemm(
             p(mx_x3[0]), p(mx_x3[1]), T3, p(row_index), MR, p(offsets), E, p(mx_w3[0]), p(mx_w3[1]),
             N3, K3, p(out["y3"]), sp), K)
         fl = 2.0 * MR * N3 * K3
         nxt["mxfp8_grouped_gemm_up"] = {"ms": round(ms, 4), "TFLOP/s": round(fl / ms / 1e9, 1),
-                                        "frac_mfma_fp8": round(fl / ms / 1e9 / MFMA_FP8_PEAK_TFS, 4), "flop": fl}
+                                        "frac_mfma_bf16": round(fl / ms / 1e9 / MFMA_F16_PEAK_TFS, 4), "flop": fl}
         del mx_x2, mx_w2, mx_x3, mx_w3
         log("next rows: %s" % nxt)
 
@@ -625,6 +636,9 @@ def main():
             "quantize_rows_protocol": ("rotated inputs >= 1 GiB, median of 10 passes" if rot
                                        else "in-step event times"),
             "quantize_rows_rotated": rot,
+            "quantize_rows_marginal_GB/s": rot["fit"]["marginal_GB/s"] if rot else None,
+            "quantize_rows_marginal_frac_hbm": rot["fit"]["marginal_frac_hbm"] if rot else None,
+            "quantize_rows_fixed_us_per_launch": rot["fit"]["fixed_us_per_launch"] if rot else None,
             "grouped_gemm_up_TFLOP/s": comps["grouped_gemm_up"]["TFLOP/s"],
             "grouped_gemm_up_frac_mfma": comps["grouped_gemm_up"]["frac_mfma"],
         },

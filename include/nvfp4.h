@@ -216,9 +216,10 @@ int nvfp4_mxfp8_quantize_rows(const uint16_t* x_bf16, int64_t rows, int64_t k, u
                               uint8_t* sc, void* stream);
 
 /*
- * MXFP8 GEMM on gfx950's scaled MFMA: Y = deq(A) . deq(B)^T with
- * deq = 2^(sc - 127) * e4m3(q) per 32-block along k, fp32 accumulation and
- * output.
+ * MXFP8 GEMM: Y = deq(A) . deq(B)^T with deq = 2^(sc - 127) * e4m3(q) per
+ * 32-block along k, fp32 accumulation and output.  Every element is decoded
+ * exactly to bf16 (an E4M3 value times a power of two) and the products,
+ * exact in fp32, are summed on the bf16 MFMA.
  *
  * Defined by: the Miles page, section MXFP8格式背景 (the format), and section
  * 配方1：端到端MXFP8 RL的设计 (forward, rollout and both gradient GEMMs run
@@ -227,12 +228,12 @@ int nvfp4_mxfp8_quantize_rows(const uint16_t* x_bf16, int64_t rows, int64_t k, u
  *
  *   a_q [m, k] u8 E4M3 codes, a_sc [m, k/32] u8 E8M0 codes (as written by
  *   nvfp4_mxfp8_quantize_rows); b_q [n, k], b_sc [n, k/32]; y [m, n] f32 out.
- *   k % 32 == 0 (k % 64 == 0 takes the fast path).  Scale code 0xFF (NaN)
- *   gives NaN outputs.
- * Accuracy: |Y - Y_ref| < 2^-9 * sum_k |a_k b_k|: the fp8 MFMA sums each
- * 32-block's products in a fixed-point window about 15 bits below the
- * block's largest product, truncating the rest (measured); block sums are
- * accumulated in fp32.
+ *   k % 32 == 0 (k % 128 == 0 with 4-byte aligned scale rows takes the fast
+ *   path).  Scale code 0xFF (NaN in E8M0; the quantizer never writes it)
+ *   gives unspecified outputs.
+ * Accuracy as nvfp4_gemm for blocks whose decoded values are bf16 numbers:
+ * every scale code from 10 to 246, which the quantizer writes for every
+ * block whose largest magnitude is at least 2^-109.
  * Errors: INVALID_VALUE, UNSUPPORTED_SHAPE (k % 32 != 0), MISALIGNED (a_q,
  * b_q, y 16 bytes), ARCH, LAUNCH.
  */
@@ -246,8 +247,8 @@ int nvfp4_mxfp8_gemm(const uint8_t* a_q, const uint8_t* a_sc, int64_t m, const u
  *   a_q [a_rows, k], a_sc [a_rows, k/32]; row_index NULL or [m_total] i32;
  *   offsets [groups+1] i32 device; b_q [groups, n, k], b_sc [groups, n, k/32];
  *   y [m_total, n] f32 out (rows at or past offsets[groups] not written).
- * groups <= 1024.  Errors as for nvfp4_grouped_gemm (k % 32 != 0 is
- * UNSUPPORTED_SHAPE).
+ * Accuracy as nvfp4_mxfp8_gemm.  groups <= 1024.  Errors as for
+ * nvfp4_grouped_gemm (k % 32 != 0 is UNSUPPORTED_SHAPE).
  */
 int nvfp4_mxfp8_grouped_gemm(const uint8_t* a_q, const uint8_t* a_sc, int64_t a_rows,
                              const int32_t* row_index, int64_t m_total, const int32_t* offsets,

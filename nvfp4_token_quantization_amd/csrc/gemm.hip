@@ -40,6 +40,8 @@
 // serves one region.  Grouped GEMMs derive the per-expert m-tile prefix from
 // the device offsets in every block, and ragged expert tiles run only their
 // non-empty 32-row slabs.
+#include <type_traits>
+
 #include "gemm_common.h"
 
 namespace nvfp4 {
@@ -283,10 +285,15 @@ __global__ __launch_bounds__(64) void gemm_rd_kernel(GemmArgs p) {
 // and the expert tile prefix (read before the K loop) the second.
 constexpr int LDS_SLAB_CODES = 32 * 64;
 constexpr int LDS_CODES = 8 * LDS_SLAB_CODES;   // one code stage buffer
-constexpr int LDS_SLAB_SCALES = 32 * 16;
-constexpr int LDS_SCALES = 8 * LDS_SLAB_SCALES;  // one scale pair buffer
 constexpr int LDS_SCALES_AT = 2 * LDS_CODES;
-constexpr int LDS_WAVE = 2 * LDS_CODES + 2 * LDS_SCALES;
+// scale bytes per row and stage pair: NVFP4 2 x 8 (16-element blocks of a
+// 128-element stage), MXFP8 2 x 2 (32-element blocks of a 64-element stage)
+template <bool MX> constexpr int lds_slab_scales() { return 32 * (MX ? 4 : 16); }
+template <bool MX> constexpr int lds_scales() { return 8 * lds_slab_scales<MX>(); }
+template <bool MX> constexpr int lds_wave() { return 2 * LDS_CODES + 2 * lds_scales<MX>(); }
+// K elements per stage (64 bytes of every row)
+template <bool MX> constexpr int lds_bk() { return MX ? 64 : 128; }
+constexpr int LDS_WAVE = lds_wave<false>();
 static_assert(LDS_WAVE * 4 <= 160 * 1024, "four waves per CU");
 
 __device__ __forceinline__ int lds_swz(int r) { return ((r >> 2) + (r & 2)) & 3; }
@@ -302,11 +309,11 @@ struct LdsOperands {
   uint32_t avalid, bvalid;  // bit i: this lane's MFMA row / column of slab i exists
 };
 
-// DMA of one K stage's codes (k0) into the code buffer at LDS address `buf`:
-// VS slabs of A, all four of B; 2 VS + 8 instructions.
+// DMA of K stage `st`'s codes (64 bytes of each row) into the code buffer at
+// LDS address `buf`: VS slabs of A, all four of B; 2 VS + 8 instructions.
 template <int VS>
-__device__ __forceinline__ void lds_issue_codes(const LdsOperands& o, uint32_t buf, uint32_t k0) {
-  const uint32_t sc = k0 / 2;
+__device__ __forceinline__ void lds_issue_codes(const LdsOperands& o, uint32_t buf, uint32_t st) {
+  const uint32_t sc = 64u * st;
 #pragma unroll
   for (int i = 0; i < VS; ++i) {
     dma16(o.aq, o.aoff[i][0], sc, buf + i * LDS_SLAB_CODES);
@@ -319,72 +326,119 @@ __device__ __forceinline__ void lds_issue_codes(const LdsOperands& o, uint32_t b
   }
 }
 
-// DMA of the scales of stages k0 / BK and k0 / BK + 1 into the scale pair
+// DMA of the scales of stages st and st + 1 (st even) into the scale pair
 // buffer at `buf`: one instruction per two slabs (lanes 0-31 the first slab's
-// rows, 32-63 the second's), four instructions.
-__device__ __forceinline__ void lds_issue_scales(const LdsOperands& o, uint32_t buf, uint32_t k0) {
-  const uint32_t ss = k0 / 16;
-  dma16(o.as, o.asoff[0], ss, buf);
-  dma16(o.as, o.asoff[1], ss, buf + 2 * LDS_SLAB_SCALES);
-  dma16(o.bs, o.bsoff[0], ss, buf + 4 * LDS_SLAB_SCALES);
-  dma16(o.bs, o.bsoff[1], ss, buf + 6 * LDS_SLAB_SCALES);
+// rows, 32-63 the second's), four instructions of 16 (NVFP4) or 4 (MXFP8)
+// bytes per lane.
+template <bool MX>
+__device__ __forceinline__ void lds_issue_scales(const LdsOperands& o, uint32_t buf, uint32_t st) {
+  constexpr int SL = lds_slab_scales<MX>();
+  if (MX) {
+    const uint32_t ss = 2u * st;
+    dma4(o.as, o.asoff[0], ss, buf);
+    dma4(o.as, o.asoff[1], ss, buf + 2 * SL);
+    dma4(o.bs, o.bsoff[0], ss, buf + 4 * SL);
+    dma4(o.bs, o.bsoff[1], ss, buf + 6 * SL);
+  } else {
+    const uint32_t ss = 8u * st;
+    dma16(o.as, o.asoff[0], ss, buf);
+    dma16(o.as, o.asoff[1], ss, buf + 2 * SL);
+    dma16(o.bs, o.bsoff[0], ss, buf + 4 * SL);
+    dma16(o.bs, o.bsoff[1], ss, buf + 6 * SL);
+  }
 }
 
 // Half a stage in the MFMA register layout: lane (li, h) holds 16-byte chunk
-// 2h + part of row li (K elements [64h + 32 part, +32)) and the dword of the
-// four block scales of its 64 elements.
+// 2h + part of row li and a dword of block scales.  NVFP4: K elements
+// [64h + 32 part, +32), and the four block scales of its 64 elements.
+// MXFP8: K elements [32h + 16 part, +16) of the stage, all in the stage's
+// 32-block h, and the row's scale dword of the stage pair (byte 2 odd + h is
+// this lane's).
 struct RegHalf {
   uint4 a[4], b[4];
   uint32_t as[4], bs[4];
 };
 
 // ds_reads of half `part` of the stage whose codes are at `buf` and whose
-// scales are the `odd` half of the pair buffer `sbuf`; rows that do not exist
-// get a zero scale, so they decode to zeros whatever their LDS bytes hold.
-template <int VS>
+// scales are the `odd` half of the pair buffer `sbuf`.  Rows that do not
+// exist must decode to zeros whatever their LDS bytes hold: NVFP4 gives them
+// a zero scale; MXFP8 (whose converter reads a zero scale as 2^-127) zero
+// codes and the scale 2^0.  Columns past n are never stored.
+template <int VS, bool MX>
 __device__ __forceinline__ void lds_read(const LdsOperands& o, const uint8_t* buf,
                                          const uint8_t* sbuf, int odd, int li, int h, int part,
                                          RegHalf& r) {
+  constexpr int SL = lds_slab_scales<MX>();
   const int c = ((2 * h + part) ^ lds_swz(li)) * 16;
-  const uint8_t* sc = sbuf + li * 16 + 8 * odd + 4 * h;
+  const uint8_t* sc = MX ? sbuf + li * 4 : sbuf + li * 16 + 8 * odd + 4 * h;
 #pragma unroll
   for (int i = 0; i < VS; ++i) {
-    r.a[i] = *reinterpret_cast<const uint4*>(buf + i * LDS_SLAB_CODES + li * 64 + c);
-    const uint32_t sv = *reinterpret_cast<const uint32_t*>(sc + i * LDS_SLAB_SCALES);
-    r.as[i] = ((o.avalid >> i) & 1u) ? sv : 0u;
+    const uint4 q = *reinterpret_cast<const uint4*>(buf + i * LDS_SLAB_CODES + li * 64 + c);
+    const uint32_t sv = *reinterpret_cast<const uint32_t*>(sc + i * SL);
+    const bool ok = (o.avalid >> i) & 1u;
+    if (MX) {
+      const uint32_t m = ok ? 0xFFFFFFFFu : 0u;
+      r.a[i] = make_uint4(q.x & m, q.y & m, q.z & m, q.w & m);
+      r.as[i] = ok ? sv : 0x7F7F7F7Fu;
+    } else {
+      r.a[i] = q;
+      r.as[i] = ok ? sv : 0u;
+    }
   }
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     r.b[j] = *reinterpret_cast<const uint4*>(buf + (4 + j) * LDS_SLAB_CODES + li * 64 + c);
-    const uint32_t sv = *reinterpret_cast<const uint32_t*>(sc + (4 + j) * LDS_SLAB_SCALES);
-    r.bs[j] = ((o.bvalid >> j) & 1u) ? sv : 0u;
+    const uint32_t sv = *reinterpret_cast<const uint32_t*>(sc + (4 + j) * SL);
+    r.bs[j] = MX ? sv : (((o.bvalid >> j) & 1u) ? sv : 0u);
   }
 }
 
-// Decode of one k-step (dword t of each 16-byte chunk, block scale byte blk)
-template <int VS>
-__device__ __forceinline__ void decode_step(const RegHalf& r, int t, int blk, f16x8 (&fa)[4],
-                                            f16x8 (&fb)[4]) {
+template <bool MX>
+using lds_op_t = typename std::conditional<MX, bf16x8, f16x8>::type;
+
+// Decode of one k-step.  NVFP4: dword t of each 16-byte chunk with block
+// scale byte blk.  MXFP8: dwords 2t and 2t + 1 with the E8M0 code in byte
+// blk of the scale dword.
+template <int VS, bool MX>
+__device__ __forceinline__ void decode_step(const RegHalf& r, int t, int blk,
+                                            lds_op_t<MX> (&fa)[4], lds_op_t<MX> (&fb)[4]) {
+  if constexpr (MX) {
 #pragma unroll
-  for (int i = 0; i < VS; ++i) fa[i] = decode8(pick(r.a[i], t), scale_pair(r.as[i], blk));
+    for (int i = 0; i < VS; ++i)
+      fa[i] = mx_decode8(t ? r.a[i].z : r.a[i].x, t ? r.a[i].w : r.a[i].y,
+                         e8m0_scale((r.as[i] >> (8 * blk)) & 0xFFu));
 #pragma unroll
-  for (int j = 0; j < 4; ++j) fb[j] = decode8(pick(r.b[j], t), scale_pair(r.bs[j], blk));
+    for (int j = 0; j < 4; ++j)
+      fb[j] = mx_decode8(t ? r.b[j].z : r.b[j].x, t ? r.b[j].w : r.b[j].y,
+                         e8m0_scale((r.bs[j] >> (8 * blk)) & 0xFFu));
+  } else {
+#pragma unroll
+    for (int i = 0; i < VS; ++i) fa[i] = decode8(pick(r.a[i], t), scale_pair(r.as[i], blk));
+#pragma unroll
+    for (int j = 0; j < 4; ++j) fb[j] = decode8(pick(r.b[j], t), scale_pair(r.bs[j], blk));
+  }
 }
 
 // One k-step: the MFMAs of the decoded operands (fa, fb) while the next
-// k-step (dword nt, scale byte nblk of `nr`) is decoded, interleaved one MFMA
-// to a few VALU instructions so the decode issues in the MFMAs' shadow.
-template <int VS>
-__device__ __forceinline__ void kstep(f32x16 (&acc)[4][4], f16x8 (&fa)[4], f16x8 (&fb)[4],
-                                      const RegHalf& nr, int nt, int nblk) {
-  f16x8 na[4], nb[4];
-  decode_step<VS>(nr, nt, nblk, na, nb);
+// k-step (nt, scale byte nblk of `nr`) is decoded, interleaved one MFMA to a
+// few VALU instructions so the decode issues in the MFMAs' shadow.
+template <int VS, bool MX>
+__device__ __forceinline__ void kstep(f32x16 (&acc)[4][4], lds_op_t<MX> (&fa)[4],
+                                      lds_op_t<MX> (&fb)[4], const RegHalf& nr, int nt, int nblk) {
+  lds_op_t<MX> na[4], nb[4];
+  decode_step<VS, MX>(nr, nt, nblk, na, nb);
 #pragma unroll
   for (int i = 0; i < VS; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[i], fb[j], acc[i][j], 0, 0, 0);
-  constexpr int NM = 4 * VS, NV = ((VS + 4) * 9 + NM - 1) / NM;
+    for (int j = 0; j < 4; ++j) {
+      if constexpr (MX)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+      else
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+    }
+  // VALU per operand decode: 9 (NVFP4: 4 converts, 4 scale multiplies, the
+  // scale pair), 6 (MXFP8: 4 converts, the scale's shift and mask)
+  constexpr int NM = 4 * VS, NV = ((VS + 4) * (MX ? 6 : 9) + NM - 1) / NM;
 #pragma unroll
   for (int m = 0; m < NM; ++m) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
@@ -396,43 +450,51 @@ __device__ __forceinline__ void kstep(f32x16 (&acc)[4][4], f16x8 (&fa)[4], f16x8
   for (int j = 0; j < 4; ++j) fb[j] = nb[j];
 }
 
-template <int VS>
+template <int VS, bool MX>
 __device__ __forceinline__ void lds_body(const GemmArgs& p, const LdsOperands& o, uint8_t* lds,
                                          int h, int li, int lane, int64_t row_lo, int64_t row_hi,
                                          int64_t n0, float rs0, float rs1) {
   constexpr int NC = 2 * VS + 8;  // code DMA instructions per stage
   constexpr int NS = 4;           // scale DMA instructions per stage pair
+  constexpr int SCALES = lds_scales<MX>();
   f32x16 acc[4][4];
 #pragma unroll
   for (int i = 0; i < VS; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = (f32x16){0};
   const uint32_t lbase = (uint32_t)(uintptr_t)lds;  // LDS address (low 32 bits)
-  const int nst = (int)(p.k / BK);                   // even and >= 2 on this path
+  const int nst = (int)(p.k / lds_bk<MX>());         // even and >= 2 on this path
   RegHalf r0, r1;
-  f16x8 fa[4], fb[4];
+  lds_op_t<MX> fa[4], fb[4];
   // stage s: codes in code buffer s & 1, scales in pair buffer (s >> 1) & 1.
   // In flight at most: codes of two stages and scales of two pairs.
-  lds_issue_scales(o, lbase + LDS_SCALES_AT, 0);
+  lds_issue_scales<MX>(o, lbase + LDS_SCALES_AT, 0);
   lds_issue_codes<VS>(o, lbase, 0);
-  lds_issue_codes<VS>(o, lbase + LDS_CODES, BK);
+  lds_issue_codes<VS>(o, lbase + LDS_CODES, 1);
   if (nst > 2) {
-    lds_issue_scales(o, lbase + LDS_SCALES_AT + LDS_SCALES, 2 * BK);
+    lds_issue_scales<MX>(o, lbase + LDS_SCALES_AT + SCALES, 2);
     wait_vmcnt<NC + NS>();  // stage 0's codes and scales are in LDS
   } else {
     wait_vmcnt<NC>();
   }
-  lds_read<VS>(o, lds, lds + LDS_SCALES_AT, 0, li, h, 0, r0);
-  decode_step<VS>(r0, 0, 0, fa, fb);
+  lds_read<VS, MX>(o, lds, lds + LDS_SCALES_AT, 0, li, h, 0, r0);
+  decode_step<VS, MX>(r0, 0, MX ? h : 0, fa, fb);
   for (int s = 0; s < nst; ++s) {
     const int cur = s & 1;
-    const uint8_t* sbuf = lds + LDS_SCALES_AT + ((s >> 1) & 1) * LDS_SCALES;
-    lds_read<VS>(o, lds + cur * LDS_CODES, sbuf, cur, li, h, 1, r1);
-    // k-steps 0..3 from r0; the last one decodes k-step 4 from r1
-    kstep<VS>(acc, fa, fb, r0, 1, 0);
-    kstep<VS>(acc, fa, fb, r0, 2, 1);
-    kstep<VS>(acc, fa, fb, r0, 3, 1);
-    kstep<VS>(acc, fa, fb, r1, 0, 2);
+    const uint8_t* sbuf = lds + LDS_SCALES_AT + ((s >> 1) & 1) * SCALES;
+    lds_read<VS, MX>(o, lds + cur * LDS_CODES, sbuf, cur, li, h, 1, r1);
+    // NVFP4: k-steps 0..3 from r0, the last decoding k-step 4 from r1.
+    // MXFP8: k-step 0 from r0, then k-step 1 decoding k-step 2 from r1;
+    // every k-step of the stage uses scale byte 2 cur + h.
+    if constexpr (MX) {
+      kstep<VS, MX>(acc, fa, fb, r0, 1, 2 * cur + h);
+      kstep<VS, MX>(acc, fa, fb, r1, 0, 2 * cur + h);
+    } else {
+      kstep<VS, MX>(acc, fa, fb, r0, 1, 0);
+      kstep<VS, MX>(acc, fa, fb, r0, 2, 1);
+      kstep<VS, MX>(acc, fa, fb, r0, 3, 1);
+      kstep<VS, MX>(acc, fa, fb, r1, 0, 2);
+    }
     // every read of stage s has been issued; once they land its code buffer
     // takes stage s + 2, and after an odd stage its scale pair buffer takes
     // the pair after next (stages s + 3, s + 4).  Stage s + 1 is in LDS once
@@ -440,30 +502,34 @@ __device__ __forceinline__ void lds_body(const GemmArgs& p, const LdsOperands& o
     wait_lgkmcnt0();
     if (s + 2 < nst) {
       if (cur && s + 3 < nst) {
-        lds_issue_scales(o, lbase + LDS_SCALES_AT + ((s >> 1) & 1) * LDS_SCALES,
-                         (uint32_t)(s + 3) * BK);
-        lds_issue_codes<VS>(o, lbase + cur * LDS_CODES, (uint32_t)(s + 2) * BK);
+        lds_issue_scales<MX>(o, lbase + LDS_SCALES_AT + ((s >> 1) & 1) * SCALES, (uint32_t)(s + 3));
+        lds_issue_codes<VS>(o, lbase + cur * LDS_CODES, (uint32_t)(s + 2));
         wait_vmcnt<NC + NS>();
       } else {
-        lds_issue_codes<VS>(o, lbase + cur * LDS_CODES, (uint32_t)(s + 2) * BK);
+        lds_issue_codes<VS>(o, lbase + cur * LDS_CODES, (uint32_t)(s + 2));
         wait_vmcnt<NC>();
       }
     } else {
       wait_vmcnt<0>();
     }
     if (s + 1 < nst)
-      lds_read<VS>(o, lds + (cur ^ 1) * LDS_CODES,
-                   lds + LDS_SCALES_AT + (((s + 1) >> 1) & 1) * LDS_SCALES, cur ^ 1, li, h, 0, r0);
-    // k-steps 4..7 from r1; the last one decodes k-step 0 of stage s + 1
+      lds_read<VS, MX>(o, lds + (cur ^ 1) * LDS_CODES,
+                       lds + LDS_SCALES_AT + (((s + 1) >> 1) & 1) * SCALES, cur ^ 1, li, h, 0, r0);
+    // the rest of the stage; the last k-step decodes k-step 0 of stage s + 1
     // (unused after the last stage)
-    kstep<VS>(acc, fa, fb, r1, 1, 2);
-    kstep<VS>(acc, fa, fb, r1, 2, 3);
-    kstep<VS>(acc, fa, fb, r1, 3, 3);
-    kstep<VS>(acc, fa, fb, r0, 0, 0);
+    if constexpr (MX) {
+      kstep<VS, MX>(acc, fa, fb, r1, 1, 2 * cur + h);
+      kstep<VS, MX>(acc, fa, fb, r0, 0, 2 * (cur ^ 1) + h);
+    } else {
+      kstep<VS, MX>(acc, fa, fb, r1, 1, 2);
+      kstep<VS, MX>(acc, fa, fb, r1, 2, 3);
+      kstep<VS, MX>(acc, fa, fb, r1, 3, 3);
+      kstep<VS, MX>(acc, fa, fb, r0, 0, 0);
+    }
   }
   // per-row epilogue scales into the last 512 bytes of LDS (every read of
   // the K loop has landed: the final k-steps consumed them)
-  float* s_rowscale = reinterpret_cast<float*>(lds + LDS_WAVE - 512);
+  float* s_rowscale = reinterpret_cast<float*>(lds + lds_wave<MX>() - 512);
   wait_lgkmcnt0();
   s_rowscale[lane] = rs0;
   s_rowscale[lane + 64] = rs1;
@@ -571,9 +637,12 @@ __device__ __forceinline__ void lds_body(const GemmArgs& p, const LdsOperands& o
   }
 }
 
-__global__ __launch_bounds__(64) void gemm_lds_kernel(GemmArgs p) {
+// One 128 x 128 tile per one-wave block.  MX: operands are MXFP8 (E4M3
+// codes, one byte per element; E8M0 scales per 32) and there is no outer
+// scale (a_s, b_s unused).
+template <bool MX>
+__device__ __forceinline__ void lds_tile(const GemmArgs& p, uint8_t* s_lds) {
   constexpr int BM = 128, BN = 128;
-  __shared__ __attribute__((aligned(16))) uint8_t s_lds[LDS_WAVE];
   static_assert(SCHED_LDS_WORDS * 4 <= LDS_CODES, "tile schedule must fit a code buffer");
   int32_t* s_prefix = reinterpret_cast<int32_t*>(s_lds + LDS_CODES);
 
@@ -584,7 +653,7 @@ __global__ __launch_bounds__(64) void gemm_lds_kernel(GemmArgs p) {
   if (!schedule_tile<BM, BN>(p.t, lane, s_prefix, tr)) return;  // block-uniform
   const int64_t row_lo = tr.row_lo, row_hi = tr.row_hi, n0 = tr.n0;
   const int g = tr.g;
-  const int64_t rowb = p.k / 2, rows_s = p.k / 16;
+  const int64_t rowb = MX ? p.k : p.k / 2, rows_s = MX ? p.k / 32 : p.k / 16;
 
   // Source A rows of the tile's 128 output rows: lane l looks up rows l and
   // 64 + l (two independent loads), every other lane's rows come by shuffle.
@@ -627,16 +696,43 @@ __global__ __launch_bounds__(64) void gemm_lds_kernel(GemmArgs p) {
   }
   // this lane's two epilogue row scales (rows lane and lane + 64), written to
   // LDS after the K loop
-  const float sbw = p.b_s[g];
-  const float rs0 = (src0 >= 0 ? p.a_s[src0] : 0.0f) * sbw;
-  const float rs1 = (src1 >= 0 ? p.a_s[src1] : 0.0f) * sbw;
+  // (MXFP8 rows without a source decode to exact zeros: their codes are masked)
+  const float sbw = MX ? 1.0f : p.b_s[g];
+  const float rs0 = MX ? 1.0f : (src0 >= 0 ? p.a_s[src0] : 0.0f) * sbw;
+  const float rs1 = MX ? 1.0f : (src1 >= 0 ? p.a_s[src1] : 0.0f) * sbw;
   const int vslabs = (int)min((int64_t)4, (row_hi - row_lo + 31) / 32);
   switch (vslabs) {
-    case 4: lds_body<4>(p, o, s_lds, h, li, lane, row_lo, row_hi, n0, rs0, rs1); break;
-    case 3: lds_body<3>(p, o, s_lds, h, li, lane, row_lo, row_hi, n0, rs0, rs1); break;
-    case 2: lds_body<2>(p, o, s_lds, h, li, lane, row_lo, row_hi, n0, rs0, rs1); break;
-    default: lds_body<1>(p, o, s_lds, h, li, lane, row_lo, row_hi, n0, rs0, rs1); break;
+    case 4: lds_body<4, MX>(p, o, s_lds, h, li, lane, row_lo, row_hi, n0, rs0, rs1); break;
+    case 3: lds_body<3, MX>(p, o, s_lds, h, li, lane, row_lo, row_hi, n0, rs0, rs1); break;
+    case 2: lds_body<2, MX>(p, o, s_lds, h, li, lane, row_lo, row_hi, n0, rs0, rs1); break;
+    default: lds_body<1, MX>(p, o, s_lds, h, li, lane, row_lo, row_hi, n0, rs0, rs1); break;
   }
+}
+
+__global__ __launch_bounds__(64) void gemm_lds_kernel(GemmArgs p) {
+  __shared__ __attribute__((aligned(16))) uint8_t s_lds[lds_wave<false>()];
+  lds_tile<false>(p, s_lds);
+}
+
+__global__ __launch_bounds__(64) void mxfp8_gemm_lds_kernel(GemmArgs p) {
+  __shared__ __attribute__((aligned(16))) uint8_t s_lds[lds_wave<true>()];
+  lds_tile<true>(p, s_lds);
+}
+
+// The MXFP8 GEMM on the one-wave LDS tile kernel when the shape allows it (k
+// a multiple of 128: whole stage pairs; 16-byte aligned codes, 4-byte aligned
+// scale rows; operands under 2 GiB); returns false otherwise.
+bool launch_mxfp8_lds(const GemmArgs& a, bool grouped, hipStream_t stream) {
+  GemmArgs p = a;
+  const int64_t lim = (int64_t)1 << 31;
+  if (p.k <= 0 || p.k % 128 != 0 || p.a_rows <= 0 || p.a_rows * p.k >= lim || p.n * p.k >= lim)
+    return false;
+  if (!nvfp4host::aligned(p.a_q, 16) || !nvfp4host::aligned(p.b_q, 16) ||
+      !nvfp4host::aligned(p.a_sb, 4) || !nvfp4host::aligned(p.b_sb, 4))
+    return false;
+  const int64_t blocks = plan_tiles<128, 128>(p.t, p.n, grouped);
+  hipLaunchKernelGGL(mxfp8_gemm_lds_kernel, dim3((unsigned)blocks), dim3(64), 0, stream, p);
+  return true;
 }
 
 template <int TM, int TN>

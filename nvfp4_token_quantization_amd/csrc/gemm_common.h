@@ -41,6 +41,24 @@ __device__ __forceinline__ f16x2 scale_pair(uint32_t scales4, int blk) {
   return as_h2((c << 7) | (c << 23));
 }
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+// E8M0 code -> the fp32 scale operand of the converter below (it uses only
+// the exponent field: code e stands for 2^(e - 127), code 0 included)
+__device__ __forceinline__ float e8m0_scale(uint32_t code) { return __uint_as_float(code << 23); }
+
+// 8 MXFP8 elements (two dwords of E4M3 codes, byte order) times their block's
+// power of two, as bf16: exact whenever the result is representable (an E4M3
+// value has at most 4 significant bits and the scale only moves the exponent)
+__device__ __forceinline__ bf16x8 mx_decode8(uint32_t w0, uint32_t w1, float scale) {
+  const bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, scale, false);
+  const bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, scale, true);
+  const bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, scale, false);
+  const bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, scale, true);
+  return (bf16x8){p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
+}
+
 __device__ __forceinline__ uint32_t pick(const uint4& v, int t) {
   return (t & 3) == 0 ? v.x : (t & 3) == 1 ? v.y : (t & 3) == 2 ? v.z : v.w;
 }
@@ -68,6 +86,11 @@ __device__ __forceinline__ void dma16(i32x4 rsrc, uint32_t voff, uint32_t soff, 
   asm volatile("s_mov_b32 m0, %3\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
                :: "v"(voff), "s"(rsrc), "s"(soff), "s"(lds) : "memory", "m0");
 }
+// 4 bytes per lane from rsrc[voff + soff] to LDS[lds + 4 * lane] (as dma16)
+__device__ __forceinline__ void dma4(i32x4 rsrc, uint32_t voff, uint32_t soff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %3\n\ts_nop 0\n\tbuffer_load_dword %0, %1, %2 offen lds"
+               :: "v"(voff), "s"(rsrc), "s"(soff), "s"(lds) : "memory", "m0");
+}
 #pragma clang diagnostic pop
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
@@ -80,5 +103,10 @@ __device__ __forceinline__ void wait_lgkmcnt0() { asm volatile("s_waitcnt lgkmcn
 // returns true, or returns false when the shape is not one it takes (the
 // caller then launches the tiled kernels).
 bool launch_gemm_skinny(const GemmArgs& a, bool grouped, hipStream_t stream);
+
+// The MXFP8 GEMM (a_q/b_q E4M3 codes, a_sb/b_sb E8M0 scales per 32, a_s and
+// b_s unused) on the LDS tile kernel: returns false when the shape or the
+// alignment is not one it takes.
+bool launch_mxfp8_lds(const GemmArgs& a, bool grouped, hipStream_t stream);
 
 }  // namespace nvfp4

@@ -1,29 +1,33 @@
-// mxfp8_gemm.hip -- dense and grouped (MoE) MXFP8 GEMM on gfx950's scaled
-// MFMA: Y[m, n] = sum over 32-blocks of 2^(e_A + e_B) * sum_32 a * b, fp32
-// accumulate and output.
+// mxfp8_gemm.hip -- entry points of the dense and grouped (MoE) MXFP8 GEMM
+// (gfx950): Y[m, n] = sum over 32-blocks of 2^(e_A + e_B) * sum_32 a * b,
+// with every product formed exactly and summed in fp32.
 //
-// MXFP8 (Miles page, section MXFP8格式背景: 32 E4M3 values per E8M0 scale)
-// maps onto v_mfma_scale_f32_32x32x64_f8f6f4 directly: the instruction takes
-// one E8M0 scale per row (A) / column (B) per 32 K-elements.  Its operand
-// layout, measured on MI355X: lane (li, h) supplies 32 bytes for row li
-// (A) or column li (B), bytes 0..15 from the MFMA's first 32-block and 16..31
-// from its second, the two lane halves h = 0, 1 splitting each block; the
-// scale of (row li, block b) comes from lane li + 32 b.  Which K positions a
-// byte stands for inside a block does not matter as long as A and B agree,
-// so lane (li, h) simply reads bytes [32 b + 16 h, +16) of each block b.
+// MXFP8 (Miles page, section MXFP8格式背景: 32 E4M3 values per E8M0 scale).
+// Each element is decoded, with its block's scale, to bf16 by
+// v_cvt_scalef32_pk_bf16_fp8 (two per instruction; the converter takes only
+// the exponent of its fp32 scale operand, which is exactly what an E8M0 scale
+// is): an E4M3 value has at most 4 significant bits, so the decoded value is
+// exact whenever it is a bf16 number, and a product of two such values is
+// exact in the fp32 accumulator of v_mfma_f32_32x32x16_bf16.  gfx950's scaled
+// fp8 MFMA would need no decode, but it sums each 32-block's products in a
+// fixed-point window about 15 bits below the block's largest product, an
+// error of up to 2^-9 sum|ab| (measured), far above the 1e-5 sum|ab| this
+// GEMM promises.
 //
-// There is no decode, so the kernel is bound by getting operands to the
-// MFMAs: four waves share a 256 x 256 block tile through LDS (below) and the
-// XCD-aware tile order of tile_sched.h keeps a region's panels in one L2.
-// Measured on the 4096 x 9728 x 2560 shape: with operand loads removed the
-// MFMAs and LDS traffic alone take 137 us; a first version whose loads were
-// each waited for before the next was issued (a mask applied right after the
-// load) ran 309 us, so masks are applied only when the data reaches LDS.
-#include "tile_sched.h"
+// The fast path (k % 128 == 0) is the one-wave LDS tile kernel of gemm.hip,
+// instantiated for MXFP8 (64-element stages, E8M0 scales per stage pair).
+// Other shapes take the kernel below: four waves share a 256 x 256 block
+// tile (each wave 128 x 128, 4 x 4 MFMA tiles) staged 128 K-elements at a
+// time through LDS by register loads, with the XCD-aware tile order of
+// tile_sched.h.  Lane (li, h) reads, for 32-block u of a stage, the 16-byte
+// chunk 2u + h of its row (A) or column (B): K positions inside a block are
+// permuted the same way for A and B, so the dot products are unchanged.
+// Loads for the next stage are issued before the current stage's MFMAs and
+// written to LDS after them (a mask applied right after each load would wait
+// for it before the next is issued).
+#include "gemm_common.h"
 
 namespace nvfp4 {
-
-typedef int i32x8 __attribute__((ext_vector_type(8)));
 
 struct MxGemmArgs {
   const uint8_t* a_q;
@@ -43,11 +47,6 @@ __device__ __forceinline__ uint4 keep_if(bool ok, const uint4& v) {
   return make_uint4(v.x & m, v.y & m, v.z & m, v.w & m);
 }
 
-__device__ __forceinline__ i32x8 mx_operand(const uint4& lo, const uint4& hi) {
-  return (i32x8){(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
-                 (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-}
-
 // Four E8M0 codes of blocks [b, b + 4) of a scale row of nblk codes; blocks
 // past the row read as 127 (2^0; their data is zero).  FULL: nblk % 4 == 0,
 // one aligned dword.
@@ -65,7 +64,7 @@ constexpr int MXL_BM = 256, MXL_BN = 256, MXL_BK = 128;
 __device__ __forceinline__ int mxl_swz(int r) { return ((r >> 1) & 7) ^ ((r & 1) << 2); }
 
 template <bool FULL>
-__global__ __launch_bounds__(256) void mxfp8_gemm_lds_kernel(MxGemmArgs p) {
+__global__ __launch_bounds__(256) void mxfp8_gemm_shared_kernel(MxGemmArgs p) {
   __shared__ int32_t s_prefix[SCHED_LDS_WORDS];
   __shared__ uint4 s_a[2][MXL_BM * MXL_BK / 16];
   __shared__ uint4 s_b[2][MXL_BN * MXL_BK / 16];
@@ -160,27 +159,36 @@ __global__ __launch_bounds__(256) void mxfp8_gemm_lds_kernel(MxGemmArgs p) {
     // above the MFMAs or hoisting both K steps' fragment reads together
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      i32x8 fa[4];
+    for (int u = 0; u < 4; ++u) {
+      // 32-block u of the stage: lane (li, h) takes 16-byte chunk 2u + h of
+      // each row (its K elements all lie in block u) and the block's E8M0
+      // code as the converter's scale
+      uint4 qa[4], qb[4];
+      float sa[4], sb[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = 128 * wm + 32 * i + li;
-        const uint4 lo = s_a[buf][r * 8 + ((4 * ks + h) ^ mxl_swz(r))];
-        const uint4 hi = s_a[buf][r * 8 + ((4 * ks + 2 + h) ^ mxl_swz(r))];
-        fa[i] = mx_operand(lo, hi);
+        qa[i] = s_a[buf][r * 8 + ((2 * u + h) ^ mxl_swz(r))];
+        sa[i] = e8m0_scale((sa_cur[i] >> (8 * u)) & 0xFFu);
       }
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int c = 128 * wn + 32 * j + li;
-        const uint4 blo = s_b[buf][c * 8 + ((4 * ks + h) ^ mxl_swz(c))];
-        const uint4 bhi = s_b[buf][c * 8 + ((4 * ks + 2 + h) ^ mxl_swz(c))];
-        const i32x8 fb = mx_operand(blo, bhi);
-        const int sbj = (int)((sb_cur[j] >> (8 * (2 * ks + h))) & 0xFFu);
+        qb[j] = s_b[buf][c * 8 + ((2 * u + h) ^ mxl_swz(c))];
+        sb[j] = e8m0_scale((sb_cur[j] >> (8 * u)) & 0xFFu);
+      }
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-              fa[i], fb, acc[i][j], 0, 0, 0, (int)((sa_cur[i] >> (8 * (2 * ks + h))) & 0xFFu), 0,
-              sbj);
+      for (int v = 0; v < 2; ++v) {
+        bf16x8 fa[4], fb[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) fa[i] = mx_decode8(v ? qa[i].z : qa[i].x, v ? qa[i].w : qa[i].y, sa[i]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) fb[j] = mx_decode8(v ? qb[j].z : qb[j].x, v ? qb[j].w : qb[j].y, sb[j]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -219,12 +227,17 @@ __global__ __launch_bounds__(256) void mxfp8_gemm_lds_kernel(MxGemmArgs p) {
 }
 
 static void launch_mx(const MxGemmArgs& a, bool grouped, hipStream_t stream) {
+  GemmArgs g{};
+  g.a_q = a.a_q; g.a_sb = a.a_sc; g.a_s = nullptr; g.a_rows = a.a_rows;
+  g.row_index = a.row_index; g.b_q = a.b_q; g.b_sb = a.b_sc; g.b_s = nullptr;
+  g.n = a.n; g.k = a.k; g.y = a.y; g.t = a.t;
+  if (launch_mxfp8_lds(g, grouped, stream)) return;
   MxGemmArgs p = a;
   const int64_t blocks = plan_tiles<MXL_BM, MXL_BN>(p.t, p.n, grouped, 1);
   if (p.k % MXL_BK == 0)
-    hipLaunchKernelGGL(mxfp8_gemm_lds_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL(mxfp8_gemm_shared_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, stream, p);
   else
-    hipLaunchKernelGGL(mxfp8_gemm_lds_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, stream,
+    hipLaunchKernelGGL(mxfp8_gemm_shared_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, stream,
                        p);
 }
 
