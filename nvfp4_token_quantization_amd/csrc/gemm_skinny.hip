@@ -296,62 +296,6 @@ __device__ __forceinline__ void skinny_item(const SkinnyArgs& p, int wave, int l
   }
 }
 
-// Grouped items come from the per-expert count of BM-row m-tiles: one wave
-// reads the expert offsets (coalesced, clamped to [0, m_total] as the tiled
-// kernels clamp them) and leaves in LDS, for each expert e < G, the first
-// m-tile s_prefix[e], its first row s_lo[e] and its end row s_hi[e]; then
-// s_prefix[G] is the number of m-tiles.
-template <int BM>
-__device__ __forceinline__ void sk_expert_prefix(const int32_t* offsets, int G, int m_total, int lane,
-                                                 int32_t* s_prefix, int32_t* s_lo, int32_t* s_hi) {
-  int32_t carry = 0;
-  for (int e0 = 0; e0 < G; e0 += 256) {  // four 64-expert segments per round of loads
-    int32_t o0[4], o1[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int e = e0 + 64 * i + lane;
-      o0[i] = offsets[min(e, G)];
-      o1[i] = offsets[min(e + 1, G)];
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int e = e0 + 64 * i + lane;
-      const int32_t lo = min(max(o0[i], 0), m_total);
-      const int32_t hi = min(max(o1[i], lo), m_total);
-      const int32_t c = e < G ? (hi - lo + BM - 1) / BM : 0;
-      int32_t incl = c;
-#pragma unroll
-      for (int d = 1; d < 64; d <<= 1) {
-        const int32_t o = __shfl_up(incl, d, 64);
-        if (lane >= d) incl += o;
-      }
-      if (e < G) {
-        s_prefix[e] = carry + incl - c;
-        s_lo[e] = lo;
-        s_hi[e] = hi;
-      }
-      carry += __shfl(incl, 63, 64);
-    }
-  }
-  if (lane == 0) s_prefix[G] = carry;
-}
-
-// The expert of m-tile mt < s_prefix[G]: the number of experts whose first
-// m-tile is at or before mt, less one (experts without m-tiles share their
-// first m-tile with the next expert that has one, so they are passed over).
-__device__ __forceinline__ int sk_find_expert(const int32_t* s_prefix, int G, int mt, int lane) {
-  int count = 0;
-  for (int e0 = 0; e0 < G; e0 += 256) {
-    int32_t v[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) v[i] = s_prefix[min(e0 + 64 * i + lane, G)];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      count += __popcll(__ballot(e0 + 64 * i + lane < G && v[i] <= mt));
-  }
-  return count - 1;
-}
-
 // AS: 16-row A slabs per item (rows per item 16 AS); TN: 16-column B slabs
 // per item; KSMAX: most waves per workgroup; NBUF: stage buffers per wave.
 // A grouped launch (one wave per workgroup; with one stage buffer at most
@@ -375,7 +319,7 @@ void gemm_skinny_kernel(SkinnyArgs p) {
   int32_t* s_hi = s_lo + G;
   int items = (int)p.items;
   if (GROUPED) {
-    if (wave == 0) sk_expert_prefix<BM>(a.t.offsets, G, m_total, lane, s_prefix, s_lo, s_hi);
+    if (wave == 0) expert_tile_prefix<BM>(a.t.offsets, G, a.t.m_total, lane, s_prefix, s_lo, s_hi);
     if (KSMAX > 1) __syncthreads();
     else wave_lds_sync();
     items = s_prefix[G] * p.nblocks;
@@ -385,7 +329,7 @@ void gemm_skinny_kernel(SkinnyArgs p) {
     const int n0 = (it - mt * p.nblocks) * 16 * TN;
     int g = 0, row_lo, row_hi;
     if (GROUPED) {
-      g = sk_find_expert(s_prefix, G, mt, lane);
+      g = find_expert(s_prefix, G, mt, lane);
       row_lo = s_lo[g] + (mt - s_prefix[g]) * BM;
       row_hi = min(s_hi[g], row_lo + BM);
     } else {

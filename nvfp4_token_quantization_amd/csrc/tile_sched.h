@@ -32,70 +32,66 @@ struct TileRange {
 };
 
 // Per-expert m-tile prefix of a contiguous per-expert layout, from the
-// device offsets, by one wave of 64 lanes: s_prefix[g] = m-tiles of BM rows
-// of the experts before g (s_prefix[G] = the total), and each expert's
-// clamped row range [lo, hi) in the two arrays after the prefix (words
-// MAX_GROUPS + 1 and 2 (MAX_GROUPS + 1) on; RANGES false: the prefix alone,
-// MAX_GROUPS + 1 words).  Offsets are clamped to
-// [0, m_total] and made non-decreasing, so bad metadata cannot address rows
-// outside the output.  The caller synchronizes before reading s_prefix.
-template <int BM, bool RANGES = true>
+// device offsets, by one wave of 64 lanes: s_prefix[e] = m-tiles of BM rows
+// of the experts before e (s_prefix[G] = the total), and each expert's
+// clamped row range [s_lo[e], s_hi[e]).  Offsets are clamped to [0, m_total]
+// and made non-decreasing, so bad metadata cannot address rows outside the
+// output.  Four 64-expert segments per round of coalesced loads (lane l reads
+// offsets e and e + 1 of expert e = 64 i + l), a wave scan per segment; all
+// arithmetic in 32 bits (offsets are int32).  The caller synchronizes before
+// reading the arrays.
+template <int BM>
 __device__ __forceinline__ void expert_tile_prefix(const int32_t* offsets, int G, int64_t m_total,
-                                                   int lane, int32_t* s_prefix) {
-  constexpr int GPT = MAX_GROUPS / 64;
-  uint32_t* s_lo = reinterpret_cast<uint32_t*>(s_prefix + (MAX_GROUPS + 1));
-  uint32_t* s_hi = reinterpret_cast<uint32_t*>(s_prefix + 2 * (MAX_GROUPS + 1));
-  // every load first (indices clamped to the G + 1 entries), so they are in
-  // flight together; a load under the per-entry condition below would wait
-  // for each one in turn
-  int32_t ov[GPT + 1];
+                                                   int lane, int32_t* s_prefix, int32_t* s_lo,
+                                                   int32_t* s_hi) {
+  const int32_t mt = (int32_t)min(m_total, (int64_t)0x7FFFFFFF);
+  int32_t carry = 0;
+  for (int e0 = 0; e0 < G; e0 += 256) {
+    int32_t o0[4], o1[4];
 #pragma unroll
-  for (int i = 0; i <= GPT; ++i) ov[i] = offsets[min(lane * GPT + i, G)];
-  int32_t local = 0;
-  int32_t cnt[GPT];
-#pragma unroll
-  for (int i = 0; i < GPT; ++i) {
-    const int gg = lane * GPT + i;
-    int32_t c = 0;
-    if (gg < G) {
-      int64_t lo = min(max((int64_t)ov[i], (int64_t)0), m_total);
-      int64_t hi = min(max((int64_t)ov[i + 1], lo), m_total);
-      c = (int32_t)((hi - lo + BM - 1) / BM);
-      if (RANGES) {
-        s_lo[gg] = (uint32_t)lo;  // m_total <= 2^31
-        s_hi[gg] = (uint32_t)hi;
-      }
+    for (int i = 0; i < 4; ++i) {  // every load first, so they are in flight together
+      const int e = e0 + 64 * i + lane;
+      o0[i] = offsets[min(e, G)];
+      o1[i] = offsets[min(e + 1, G)];
     }
-    cnt[i] = c;
-    local += c;
-  }
-  int32_t incl = local;
 #pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    int32_t o = __shfl_up(incl, d, 64);
-    if (lane >= d) incl += o;
-  }
-  int32_t run = incl - local;
+    for (int i = 0; i < 4; ++i) {
+      const int e = e0 + 64 * i + lane;
+      const int32_t lo = min(max(o0[i], 0), mt);
+      const int32_t hi = min(max(o1[i], lo), mt);
+      const int32_t c = e < G ? (int32_t)(((uint32_t)(hi - lo) + (BM - 1)) / BM) : 0;
+      int32_t incl = c;
 #pragma unroll
-  for (int i = 0; i < GPT; ++i) {
-    const int gg = lane * GPT + i;
-    if (gg <= G) s_prefix[gg] = run;
-    run += cnt[i];
+      for (int d = 1; d < 64; d <<= 1) {
+        const int32_t o = __shfl_up(incl, d, 64);
+        if (lane >= d) incl += o;
+      }
+      if (e < G) {
+        s_prefix[e] = carry + incl - c;
+        s_lo[e] = lo;
+        s_hi[e] = hi;
+      }
+      carry += __shfl(incl, 63, 64);
+    }
   }
-  // the loop covers entries 0..MAX_GROUPS - 1; with G == MAX_GROUPS the
-  // total (entry G) is the last lane's final running sum
-  if (G == MAX_GROUPS && lane == 63) s_prefix[MAX_GROUPS] = run;
+  if (lane == 0) s_prefix[G] = carry;
 }
 
-// The expert that owns global m-tile mt (mt < s_prefix[G]): the last g with
-// s_prefix[g] <= mt, so experts without tiles are skipped.
-__device__ __forceinline__ int find_expert(const int32_t* s_prefix, int G, int64_t mt) {
-  int lo = 0, hi = G - 1;
-  while (lo < hi) {
-    int mid = (lo + hi + 1) >> 1;
-    if (s_prefix[mid] <= mt) lo = mid; else hi = mid - 1;
+// The expert that owns m-tile mt < s_prefix[G]: the number of experts whose
+// first m-tile is at or before mt, less one (experts without m-tiles share
+// their first m-tile with the next expert that has one, so they are passed
+// over).  Called by all 64 lanes of a wave.
+__device__ __forceinline__ int find_expert(const int32_t* s_prefix, int G, int mt, int lane) {
+  int count = 0;
+  for (int e0 = 0; e0 < G; e0 += 256) {
+    int32_t v[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = s_prefix[min(e0 + 64 * i + lane, G)];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      count += __popcll(__ballot(e0 + 64 * i + lane < G && v[i] <= mt));
   }
-  return lo;
+  return count - 1;
 }
 
 // A readable int32 for the gathered-row load below when there is no index
@@ -128,61 +124,60 @@ template <int BM, int BN>
 __device__ __forceinline__ bool schedule_tile(const TileGrid& t, int lane,
                                               int32_t* s_prefix /* SCHED_LDS_WORDS */,
                                               TileRange& out) {
-  const int xcd = blockIdx.x % 8;
-  const int64_t jloc = blockIdx.x / 8;
+  // tile counts and indices fit in 32 bits; 64-bit divisions by run-time
+  // values are long software sequences here
+  const int xcd = (int)(blockIdx.x % 8);
+  const int jloc = (int)(blockIdx.x / 8);
   const int xn = xcd % t.xcd_n, xm = xcd / t.xcd_n, XM = 8 / t.xcd_n;
-  const int64_t npx = (t.tiles_n + t.xcd_n - 1) / t.xcd_n;
-  const int64_t nlo = xn * npx, nhi = min((int64_t)t.tiles_n, nlo + npx);
+  const int npx = (t.tiles_n + t.xcd_n - 1) / t.xcd_n;
+  const int nlo = xn * npx, nhi = min(t.tiles_n, nlo + npx);
   if (nlo >= nhi) return false;  // block-uniform
-  const int64_t width = nhi - nlo;
+  const int width = nhi - nlo;
   // Region tiles are issued in order; when the last round of a region would
   // leave more than half of the XCD's slots idle, its tiles are issued as
   // two halves of BM / 2 rows so that round takes about half as long.
-  auto place = [&](int64_t mcount, int64_t& jf, int& hf) -> bool {
-    const int64_t T = mcount * width;
-    const int64_t tail = T % t.slots;
-    const int64_t split = (tail != 0 && 2 * tail <= t.slots) ? tail : 0;
-    const int64_t F = T - split;
+  auto place = [&](int mcount, int& jf, int& hf) -> bool {
+    const int T = mcount * width;
+    const int tail = T % t.slots;
+    const int split = (tail != 0 && 2 * tail <= t.slots) ? tail : 0;
+    const int F = T - split;
     if (jloc < F) {
       jf = jloc;
       hf = -1;
       return true;
     }
-    const int64_t hidx = jloc - F;
+    const int hidx = jloc - F;
     if (hidx >= 2 * split) return false;
     jf = F + hidx / 2;
-    hf = (int)(hidx & 1);
+    hf = hidx & 1;
     return true;
   };
-  int64_t jf = 0, mt, nt;
-  int hf = -1;
+  int jf = 0, hf = -1, mt, nt;
   int64_t row_lo, row_hi;
   int g = 0;
   if (t.offsets) {
     const int G = t.groups;
-    const uint32_t* s_lo = reinterpret_cast<const uint32_t*>(s_prefix + (MAX_GROUPS + 1));
-    const uint32_t* s_hi = reinterpret_cast<const uint32_t*>(s_prefix + 2 * (MAX_GROUPS + 1));
-    expert_tile_prefix<BM>(t.offsets, G, t.m_total, lane, s_prefix);
+    int32_t* s_lo = s_prefix + (MAX_GROUPS + 1);
+    int32_t* s_hi = s_prefix + 2 * (MAX_GROUPS + 1);
+    expert_tile_prefix<BM>(t.offsets, G, t.m_total, lane, s_prefix, s_lo, s_hi);
     __syncthreads();
-    const int64_t total_mt = s_prefix[G];
-    const int64_t mpx = (total_mt + XM - 1) / XM;
-    const int64_t mcount = min(mpx, max(total_mt - xm * mpx, (int64_t)0));
+    const int total_mt = s_prefix[G];
+    const int mpx = (total_mt + XM - 1) / XM;
+    const int mcount = min(mpx, max(total_mt - xm * mpx, 0));
     if (!place(mcount, jf, hf)) return false;  // block-uniform
     mt = xm * mpx + jf / width;
     nt = nlo + jf % width;
-    g = find_expert(s_prefix, G, mt);
-    const int64_t glo = (int64_t)s_lo[g];
-    const int64_t ghi = (int64_t)s_hi[g];
-    row_lo = glo + (mt - s_prefix[g]) * BM;
-    row_hi = min(ghi, row_lo + BM);
+    g = find_expert(s_prefix, G, mt, lane);
+    row_lo = (int64_t)s_lo[g] + (int64_t)(mt - s_prefix[g]) * BM;
+    row_hi = min((int64_t)s_hi[g], row_lo + BM);
   } else {
-    const int64_t tiles_m = (t.m_total + BM - 1) / BM;
-    const int64_t mpx = (tiles_m + XM - 1) / XM;
-    const int64_t mcount = min(mpx, max(tiles_m - xm * mpx, (int64_t)0));
+    const int tiles_m = (int)((t.m_total + BM - 1) / BM);
+    const int mpx = (tiles_m + XM - 1) / XM;
+    const int mcount = min(mpx, max(tiles_m - xm * mpx, 0));
     if (!place(mcount, jf, hf)) return false;  // block-uniform
     mt = xm * mpx + jf / width;
     nt = nlo + jf % width;
-    row_lo = mt * BM;
+    row_lo = (int64_t)mt * BM;
     row_hi = min(t.m_total, row_lo + BM);
   }
   if (hf >= 0) {  // half tile: rows [row_lo + (BM/2) hf, row_lo + (BM/2)(hf + 1))
@@ -192,7 +187,7 @@ __device__ __forceinline__ bool schedule_tile(const TileGrid& t, int lane,
   if (row_lo >= row_hi) return false;  // block-uniform (never for a consistent prefix)
   out.row_lo = row_lo;
   out.row_hi = row_hi;
-  out.n0 = nt * BN;
+  out.n0 = (int64_t)nt * BN;
   out.g = g;
   return true;
 }
