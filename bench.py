@@ -28,7 +28,11 @@ Traffic counters (profiles/traffic.json, used for roofline.traffic):
       python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline --no-next
   the same two counters over `python3 bench.py --calib-copy` (a plain 1 GiB
   device copy), then
-  python bench.py --pmc-summary FETCH_DIR WRITE_DIR CALIB_FETCH_DIR CALIB_WRITE_DIR
+  and, for the rollout-decode rows, the two counters over
+      python3 bench.py --steps 1 --warmup 0 --no-cpu-baseline --no-next --decode-counters
+  then
+  python bench.py --pmc-summary FETCH_DIR WRITE_DIR CALIB_FETCH_DIR CALIB_WRITE_DIR \
+      [DECODE_FETCH_DIR DECODE_WRITE_DIR]
 """
 import argparse
 import hashlib
@@ -53,14 +57,21 @@ T0 = time.time()
 
 # Source files each timed kernel is built from (its traffic counters stay
 # valid until one of these changes).
-_QUANT_SRC = ("quantize.hip", "nvfp4_internal.h", "abi_common.hip")
-_GEMM_SRC = ("gemm.hip", "tile_sched.h", "nvfp4_internal.h", "abi_common.hip")
+_QUANT_SRC = ("quantize.hip", "nvfp4_internal.h", "host_util.hip")
+_GEMM_SRC = ("gemm.hip", "gemm_common.h", "tile_sched.h", "nvfp4_internal.h", "host_util.hip")
+_SKINNY_SRC = ("gemm_skinny.hip", "gemm_common.h", "tile_sched.h", "nvfp4_internal.h", "host_util.hip")
 KERNEL_SOURCES = {
     "quantize_weight_dense": _QUANT_SRC, "quantize_weight_up": _QUANT_SRC,
     "quantize_weight_down": _QUANT_SRC, "quantize_rows_dense": _QUANT_SRC,
     "quantize_rows_moe": _QUANT_SRC, "requantize_rows_amax_reuse": _QUANT_SRC,
     "gemm_dense": _GEMM_SRC, "grouped_gemm_up": _GEMM_SRC, "grouped_gemm_down": _GEMM_SRC,
+    "decode_gemm_dense": _SKINNY_SRC, "decode_grouped_gemm_up": _SKINNY_SRC,
+    "decode_grouped_gemm_down": _SKINNY_SRC,
 }
+# rollout-decode rows under `--decode-counters`: each runs DECODE_REPS times on
+# the few-rows kernel, in this order
+DECODE_ROWS = ["decode_gemm_dense", "decode_grouped_gemm_up", "decode_grouped_gemm_down"]
+DECODE_REPS = 3
 
 
 def kernel_digest(name):
@@ -132,13 +143,16 @@ def _pmc_dispatches(csv_dir, counter):
     return [(k, v[0], v[1], v[2]) for k, v in sorted(acc.items())]
 
 
-def pmc_summary(fetch_dir, write_dir, cfetch_dir, cwrite_dir, path=None):
+def pmc_summary(fetch_dir, write_dir, cfetch_dir, cwrite_dir, dfetch_dir=None, dwrite_dir=None,
+                path=None):
     """Per-launch HBM bytes of every step launch from FETCH_SIZE and
     WRITE_SIZE runs of this bench, each scaled by the same counter's reading
-    for a plain copy of CALIB_BYTES; writes `path` (default
-    profiles/traffic.json) and returns the summary."""
+    for a plain copy of CALIB_BYTES (and of the rollout-decode rows from the
+    two counters over a `--decode-counters` run, when given); writes `path`
+    (default profiles/traffic.json) and returns the summary."""
     out = {"calibration": {}, "kernels": {}}
     per = {}
+    factors = {}
     for counter, ddir, cdir in (("FETCH_SIZE", fetch_dir, cfetch_dir),
                                 ("WRITE_SIZE", write_dir, cwrite_dir)):
         cal = [d for d in _pmc_dispatches(cdir, counter) if "nvfp4" not in d[1]]
@@ -146,6 +160,7 @@ def pmc_summary(fetch_dir, write_dir, cfetch_dir, cwrite_dir, path=None):
         factor = (CALIB_BYTES / 1024.0) / big[3]
         out["calibration"][counter] = {"copy_kernel": big[1], "copy_bytes": CALIB_BYTES,
                                        "counter_KiB": big[3], "factor": factor}
+        factors[counter] = factor
         # the step's launches (the MoE layout is routed once, before the steps)
         disp = [d for d in _pmc_dispatches(ddir, counter) if "nvfp4" in d[1] and "route_" not in d[1]]
         n_per_step = sum(c for _, c in STEP_LAUNCHES)
@@ -159,6 +174,15 @@ def pmc_summary(fetch_dir, write_dir, cfetch_dir, cwrite_dir, path=None):
                 kib = sum(d[3] for d in disp[i:i + cnt])
                 per.setdefault(name, {}).setdefault(counter, []).append(kib * 1024.0 * factor)
                 i += cnt
+    if dfetch_dir and dwrite_dir:
+        for counter, ddir in (("FETCH_SIZE", dfetch_dir), ("WRITE_SIZE", dwrite_dir)):
+            disp = [d for d in _pmc_dispatches(ddir, counter) if "gemm_skinny_kernel" in d[1]]
+            if len(disp) != len(DECODE_ROWS) * DECODE_REPS:
+                raise SystemExit("%s: %d few-rows dispatches, expected %d" %
+                                 (counter, len(disp), len(DECODE_ROWS) * DECODE_REPS))
+            for i, name in enumerate(DECODE_ROWS):
+                for d in disp[i * DECODE_REPS:(i + 1) * DECODE_REPS]:
+                    per.setdefault(name, {}).setdefault(counter, []).append(d[3] * 1024.0 * factors[counter])
     for name, d in per.items():
         f = sum(d["FETCH_SIZE"]) / len(d["FETCH_SIZE"])
         w = sum(d["WRITE_SIZE"]) / len(d["WRITE_SIZE"])
@@ -175,7 +199,7 @@ def main():
     if len(sys.argv) > 1 and sys.argv[1] == "--calib-copy":
         return calib_copy()
     if len(sys.argv) > 1 and sys.argv[1] == "--pmc-summary":
-        pmc_summary(*sys.argv[2:6])
+        pmc_summary(*sys.argv[2:8])
         return None
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -186,6 +210,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-next", action="store_true",
                     help="skip the separately timed rows (used by the counter runs)")
+    ap.add_argument("--decode-counters", action="store_true",
+                    help="after the steps run only the rollout-decode rows, %d launches each "
+                         "and untimed (the counter runs for those rows)" % DECODE_REPS)
     ap.add_argument("--cpu-sample-rows", type=int, default=4096)
     ap.add_argument("--cpu-sample-entries", type=int, default=30000000)
     args = ap.parse_args()
@@ -449,7 +476,7 @@ def main():
     # weights are the step's quantized tensors (same shapes and distribution),
     # copied so the rotation covers >= 1 GiB.
     decode = {}
-    if not args.no_next:
+    if not args.no_next or args.decode_counters:
         d5 = sg.workload(5, part={"x", "h", "xd", "logits"})
         xq5 = nv.nvfp4_quantize_rows(up(d5["x"]))
         hq5 = nv.nvfp4_quantize_rows(up(d5["h"]), amax_in=up(d5["h_amax"]))
@@ -478,7 +505,7 @@ def main():
         }
         for name, c in cases.items():
             wfoot = sum(t.numel() * t.element_size() for t in c["w"])
-            R = rotations(wfoot)
+            R = 1 if args.decode_counters else rotations(wfoot)
             sets = [(tuple(t.clone() for t in c["w"]), empty((c["m_out"], c["n"]), f32)) for _ in range(R)]
             if name == "decode_gemm_dense":
                 fns = [(lambda w=w, y=y: L.nvfp4_gemm(
@@ -492,6 +519,14 @@ def main():
                 fns = [(lambda w=w, y=y: L.nvfp4_grouped_gemm(
                     p(hq5[0]), p(hq5[1]), p(hq5[2]), MR5, None, MR5, p(off5), E,
                     p(w[0]), p(w[1]), p(w[2]), N4, K4, p(y), sp)) for w, y in sets]
+            if args.decode_counters:
+                for _ in range(DECODE_REPS):
+                    st = fns[0]()
+                    if st != 0:
+                        raise RuntimeError("%s failed: %s" % (name, nv.status_string(st)))
+                torch.cuda.synchronize()
+                decode[name] = {"bytes": int(c["bytes"]), "launches": DECODE_REPS}
+                continue
             ms = time_rotated(fns)
             gbs = c["bytes"] / (ms * 1e-3) / 1e9
             decode[name] = {"ms": round(ms, 4), "GB/s": round(gbs, 1), "frac_hbm": round(gbs / HBM_PEAK_GBS, 4),
@@ -600,6 +635,10 @@ def main():
             e = tr.get(hdom)
             if e and e.get("source_digest") == kernel_digest(hdom):
                 roof_hbm["traffic"] = e["bytes_per_launch"]
+            for n in DECODE_ROWS:
+                e = tr.get(n)
+                if n in decode and "ms" in decode[n] and e and e.get("source_digest") == kernel_digest(n):
+                    decode[n]["traffic"] = e["bytes_per_launch"]
         except (ValueError, KeyError):
             pass
 
