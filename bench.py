@@ -20,16 +20,20 @@ run of the same K steps with HIP events recorded on the launch stream around
 every launch; each kernel's achieved GB/s or TFLOP/s is its algorithmic bytes
 or flops (stated in the design notes) over that duration.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-next]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--settle-ms T] [--no-cpu-baseline]
+       [--no-next]
+Before the W warm-up steps the step runs untimed for at least T ms (default
+150): the shader clock needs some tens of milliseconds of load to settle,
+and the first milliseconds run up to 20% slow.
 Prints one JSON line on stdout; progress goes to stderr.
 
 Traffic counters (profiles/traffic.json, used for roofline.traffic):
   rocprofv3 --pmc FETCH_SIZE (then WRITE_SIZE) --output-format csv -d DIR -- \
-      python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline --no-next
+      python3 bench.py --steps 2 --warmup 1 --settle-ms 0 --no-cpu-baseline --no-next
   the same two counters over `python3 bench.py --calib-copy` (a plain 1 GiB
   device copy), then
   and, for the rollout-decode rows, the two counters over
-      python3 bench.py --steps 1 --warmup 0 --no-cpu-baseline --no-next --decode-counters
+      python3 bench.py --steps 1 --warmup 0 --settle-ms 0 --no-cpu-baseline --no-next --decode-counters
   then
   python bench.py --pmc-summary FETCH_DIR WRITE_DIR CALIB_FETCH_DIR CALIB_WRITE_DIR \
       [DECODE_FETCH_DIR DECODE_WRITE_DIR]
@@ -207,6 +211,9 @@ def main():
     # the shader clock takes some tens of milliseconds of load to settle; the
     # first few milliseconds of launches run up to 20% slow
     ap.add_argument("--warmup", type=int, default=30)
+    ap.add_argument("--settle-ms", type=float, default=150.0,
+                    help="before the warm-up steps, run whole untimed steps for at least this "
+                         "long, so the timed steps see a settled clock whatever --warmup is")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-next", action="store_true",
                     help="skip the separately timed rows (used by the counter runs)")
@@ -349,6 +356,14 @@ def main():
                 events[j][1].record(stream)
 
     names = [n for n, _ in launches(0)]
+    settle_steps, t_settle = 0, time.time()
+    while (time.time() - t_settle) * 1e3 < args.settle_ms:
+        run_step(settle_steps)
+        settle_steps += 1
+        if settle_steps % 16 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    log("settle: %d untimed steps in %.0f ms" % (settle_steps, (time.time() - t_settle) * 1e3))
     log("warmup %d steps" % args.warmup)
     for i in range(args.warmup):
         run_step(i)
@@ -655,6 +670,7 @@ def main():
         "n_gpus": 1,
         "steps": K,
         "warmup": args.warmup,
+        "settle_steps": settle_steps,
         "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True,
         "scaling": "weak",
