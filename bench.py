@@ -71,11 +71,15 @@ KERNEL_SOURCES = {
     "gemm_dense": _GEMM_SRC, "grouped_gemm_up": _GEMM_SRC, "grouped_gemm_down": _GEMM_SRC,
     "decode_gemm_dense": _SKINNY_SRC, "decode_grouped_gemm_up": _SKINNY_SRC,
     "decode_grouped_gemm_down": _SKINNY_SRC,
+    "grouped_gemm_up_swiglu": _GEMM_SRC + ("swiglu_core.h",),
 }
 # rollout-decode rows under `--decode-counters`: each runs DECODE_REPS times on
 # the few-rows kernel, in this order
 DECODE_ROWS = ["decode_gemm_dense", "decode_grouped_gemm_up", "decode_grouped_gemm_down"]
 DECODE_REPS = 3
+# launches run DECODE_REPS times after the decode rows under `--decode-counters`
+# (row name, kernel name in the trace)
+EXTRA_COUNTER_ROWS = [("grouped_gemm_up_swiglu", "gemm_lds_swiglu_kernel")]
 
 
 def kernel_digest(name):
@@ -186,6 +190,13 @@ def pmc_summary(fetch_dir, write_dir, cfetch_dir, cwrite_dir, dfetch_dir=None, d
                                  (counter, len(disp), len(DECODE_ROWS) * DECODE_REPS))
             for i, name in enumerate(DECODE_ROWS):
                 for d in disp[i * DECODE_REPS:(i + 1) * DECODE_REPS]:
+                    per.setdefault(name, {}).setdefault(counter, []).append(d[3] * 1024.0 * factors[counter])
+            for name, kern in EXTRA_COUNTER_ROWS:
+                disp = [d for d in _pmc_dispatches(ddir, counter) if kern in d[1]]
+                if len(disp) != DECODE_REPS:
+                    raise SystemExit("%s: %d %s dispatches, expected %d" % (counter, len(disp), kern,
+                                                                          DECODE_REPS))
+                for d in disp:
                     per.setdefault(name, {}).setdefault(counter, []).append(d[3] * 1024.0 * factors[counter])
     for name, d in per.items():
         f = sum(d["FETCH_SIZE"]) / len(d["FETCH_SIZE"])
@@ -551,6 +562,23 @@ def main():
             torch.cuda.empty_cache()
         decode["routing"] = {"tokens": MD, "routed_rows": MR5, "experts_with_rows": e_act,
                              "max_rows_per_expert": int(counts5.max())}
+        if args.decode_counters:
+            # the up GEMM with SwiGLU in its epilogue (the step's X and W_up)
+            q3, w3 = out["x3"], out["w3"]
+            hsw = empty((MR, N3 // 2), torch.bfloat16)
+            amsw = empty((MR,), f32)
+            for _ in range(DECODE_REPS):
+                st = L.nvfp4_grouped_gemm_swiglu(
+                    p(q3[0]), p(q3[1]), p(q3[2]), T3, p(row_index), MR, p(offsets), E,
+                    p(w3[0]), p(w3[1]), p(w3[2]), N3 // 2, K3, p(hsw), p(amsw), sp)
+                if st != 0:
+                    raise RuntimeError("grouped_gemm_up_swiglu failed: %s" % nv.status_string(st))
+            torch.cuda.synchronize()
+            decode["grouped_gemm_up_swiglu"] = {
+                "bytes": int(T3 * (K3 // 2 + K3 // 16 + 4) + E * (N3 * (K3 // 2 + K3 // 16) + 4) +
+                             MR * (N3 // 2) * 2 + MR * 4),
+                "launches": DECODE_REPS}
+            del hsw, amsw
         log("decode (skinny) shapes: %s" % decode)
 
     if not args.no_next:
@@ -564,6 +592,39 @@ def main():
         nxt["swiglu_quantize_chained"] = {"ms": round(ms, 4), "GB/s": round(byt / ms / 1e6, 1),
                                           "frac_hbm": round(byt / ms / 1e6 / HBM_PEAK_GBS, 4),
                                           "bytes": int(byt)}
+        # the whole MoE up block, X -> H quantized, two ways: the up GEMM's fp32
+        # output then the fused SwiGLU -> requantize kernel, against SwiGLU in
+        # the up GEMM's epilogue (bf16 H and its amax) then the requantize with
+        # amax reuse.  Both end with the same codes (tested).
+        q3 = out["x3"]
+        w3 = out["w3"]
+        hsw = empty((MR, FH), torch.bfloat16)
+        amsw = empty((MR,), f32)
+        qsw = (empty((MR, FH // 2), u8), empty((MR, FH // 16), u8), empty((MR,), f32))
+
+        def chain_unfused():
+            L.nvfp4_grouped_gemm(p(q3[0]), p(q3[1]), p(q3[2]), T3, p(row_index), MR, p(offsets), E,
+                                 p(w3[0]), p(w3[1]), p(w3[2]), N3, K3, p(out["y3"]), sp)
+            return L.nvfp4_swiglu_quantize_rows(p(out["y3"]), MR, FH, None, None, p(qsw[0]),
+                                                p(qsw[1]), p(qsw[2]), sp)
+
+        def chain_fused():
+            L.nvfp4_grouped_gemm_swiglu(p(q3[0]), p(q3[1]), p(q3[2]), T3, p(row_index), MR, p(offsets),
+                                        E, p(w3[0]), p(w3[1]), p(w3[2]), FH, K3, p(hsw), p(amsw), sp)
+            return L.nvfp4_quantize_rows(p(hsw), MR, FH, p(amsw), p(qsw[0]), p(qsw[1]), p(qsw[2]), sp)
+
+        fl_up = 2.0 * MR * N3 * K3
+        for name, fn in (("moe_up_block_unfused", chain_unfused), ("moe_up_block_fused", chain_fused)):
+            ms = time_extra(fn, K)
+            nxt[name] = {"ms": round(ms, 4), "TFLOP/s": round(fl_up / ms / 1e9, 1),
+                         "frac_mfma": round(fl_up / ms / 1e9 / MFMA_F16_PEAK_TFS, 4), "flop": fl_up}
+        ms = time_extra(lambda: L.nvfp4_grouped_gemm_swiglu(
+            p(q3[0]), p(q3[1]), p(q3[2]), T3, p(row_index), MR, p(offsets), E, p(w3[0]), p(w3[1]),
+            p(w3[2]), FH, K3, p(hsw), p(amsw), sp), K)
+        nxt["grouped_gemm_up_swiglu"] = {"ms": round(ms, 4), "TFLOP/s": round(fl_up / ms / 1e9, 1),
+                                         "frac_mfma": round(fl_up / ms / 1e9 / MFMA_F16_PEAK_TFS, 4),
+                                         "flop": fl_up}
+        del hsw, amsw, qsw
         # on-device routing of the MoE batch (4096 tokens x 128 logits -> top-8
         # contiguous layout: experts, offsets, row_index, slot_of)
         rbuf = {k: torch.empty_like(v) for k, v in rt3.items()}

@@ -311,6 +311,47 @@ int nvfp4_grouped_gemm(const uint8_t* a_q, const uint8_t* a_sb, const float* a_s
                        int64_t groups, const uint8_t* b_q, const uint8_t* b_sb, const float* b_s,
                        int64_t n, int64_t k, float* y, void* stream);
 
+/*
+ * Grouped (MoE) up-projection with SwiGLU in the epilogue: the fused gate|up
+ * GEMM of nvfp4_grouped_gemm, but instead of the fp32 output Y [m_total, 2f]
+ * it writes H = silu(gate) * up as bf16 and the row amax of H, the input of
+ * the per-token requantize with amax reuse (nvfp4_quantize_rows with
+ * amax_in = amax gives the same bits as quantizing H afresh).
+ *
+ * Defined by: "miniTE报告" section Transformer Engine路径优化 (fusion and amax
+ * reuse around the low-precision GEMMs), the Miles page, section
+ * 并行度与张量转换的一致性契约 (gate and up as one fused GEMM under one FP32
+ * scale) and section 实验结果 item 10 (work fused into the GEMM epilogue).
+ *
+ *   A, row_index, offsets, groups: as nvfp4_grouped_gemm.
+ *   B: b_q [groups, 2f, k/2], b_sb [groups, 2f, k/16], b_s [groups]: rows
+ *      [0, f) of each expert are gate, rows [f, 2f) up.
+ *   h    [m_total, f] bf16 out: h = bf16(fl32(g u / (1 + e^-g))) with the
+ *        arithmetic of nvfp4_swiglu_quantize_rows, where g = Y[row, c] and
+ *        u = Y[row, f + c] are the fused GEMM's fp32 outputs (accuracy as
+ *        nvfp4_grouped_gemm; bit-identical to what nvfp4_grouped_gemm writes
+ *        whenever that call takes its tiled kernel, i.e. more than 16 routed
+ *        rows per expert on average).  Rows at or past offsets[groups] are
+ *        not written.
+ *   amax [m_total] f32 out: the largest |h| of each row (0 for rows past
+ *        offsets[groups]).  Set to zero, then raised by atomic maxima of
+ *        the bit patterns (the result does not depend on their order).
+ * k must be a positive multiple of 256; 2f < 2^22.
+ * Cost: it moves about 117 MB less HBM traffic than nvfp4_grouped_gemm plus
+ * nvfp4_swiglu_quantize_rows on the MoE up-projection (and needs no fp32
+ * output buffer), but on MI355X it takes longer: the SwiGLU arithmetic runs
+ * in each tile's epilogue at one wave per SIMD, where the separate
+ * HBM-bound SwiGLU kernel hides it behind memory traffic.
+ * Errors: INVALID_VALUE, UNSUPPORTED_SHAPE (k, f or groups out of range),
+ * MISALIGNED (codes and block scales 16 bytes, h 2, the rest 4), ARCH,
+ * LAUNCH.
+ */
+int nvfp4_grouped_gemm_swiglu(const uint8_t* a_q, const uint8_t* a_sb, const float* a_s,
+                              int64_t a_rows, const int32_t* row_index, int64_t m_total,
+                              const int32_t* offsets, int64_t groups, const uint8_t* b_q,
+                              const uint8_t* b_sb, const float* b_s, int64_t f, int64_t k,
+                              uint16_t* h, float* amax, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

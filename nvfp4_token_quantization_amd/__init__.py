@@ -13,6 +13,7 @@ Functions keep the C names:
   nvfp4_quantize_weight(w, amax_in=None)          -> (q, sb, s, amax)
   nvfp4_gemm(a, b)                                -> y
   nvfp4_grouped_gemm(a, offsets, b, row_index=None, m_total=None) -> y
+  nvfp4_grouped_gemm_swiglu(a, offsets, b, row_index=None, m_total=None) -> (h, amax)
 
 (The codec self-test hooks live in the test-only ``selftest`` submodule over
 ``libnvfp4_selftest.so``.)
@@ -56,6 +57,8 @@ def lib():
         L.nvfp4_quantize_weight.argtypes = [P, I64, I64, I64, P, P, P, P, P, P]
         L.nvfp4_gemm.argtypes = [P, P, P, I64, P, P, P, I64, I64, P, P]
         L.nvfp4_grouped_gemm.argtypes = [P, P, P, I64, P, I64, P, I64, P, P, P, I64, I64, P, P]
+        L.nvfp4_grouped_gemm_swiglu.argtypes = [P, P, P, I64, P, I64, P, I64, P, P, P, I64, I64,
+                                                P, P, P]
         L.nvfp4_swiglu_quantize_rows.argtypes = [P, I64, I64, P, P, P, P, P, P]
         L.nvfp4_moe_route.argtypes = [P, I64, I64, I64, P, P, P, P, P]
         L.nvfp4_dequantize_rows.argtypes = [P, P, P, I64, I64, I64, P, P]
@@ -65,7 +68,7 @@ def lib():
         for f in ("nvfp4_quantize_rows", "nvfp4_quantize_weight", "nvfp4_gemm",
                   "nvfp4_swiglu_quantize_rows", "nvfp4_moe_route", "nvfp4_dequantize_rows",
                   "nvfp4_mxfp8_quantize_rows", "nvfp4_mxfp8_gemm", "nvfp4_mxfp8_grouped_gemm",
-                  "nvfp4_grouped_gemm"):
+                  "nvfp4_grouped_gemm", "nvfp4_grouped_gemm_swiglu"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -438,3 +441,46 @@ def nvfp4_grouped_gemm(a, offsets, b, row_index=None, m_total=None, out=None):
                                   n, k, _ptr(y), _stream(dev))
     _check("nvfp4_grouped_gemm", st)
     return y
+
+
+def nvfp4_grouped_gemm_swiglu(a, offsets, b, row_index=None, m_total=None, out=None):
+    """Grouped up-projection with SwiGLU in the epilogue.
+
+    a, offsets, row_index, m_total as nvfp4_grouped_gemm; b = the fused
+    gate|up weight (q [groups, 2f, k/2], sb [groups, 2f, k/16], s [groups]),
+    gate rows first.  Returns (h bf16 [m_total, f], amax float32 [m_total]):
+    H = silu(gate) * up of the GEMM output and its row amax (the amax_in of
+    the requantize).  out: optional preallocated (h, amax).  k must be a
+    positive multiple of 256.
+    """
+    aq, asb, as_ = _operand(a, "a", 2, a[0].shape[0] if a[0].dim() == 2 else -1)
+    if b[0].dim() != 3:
+        raise ValueError("b.q must be [groups, 2f, k/2]")
+    bq, bsb, bs = _operand(b, "b", 3, b[0].shape[0])
+    _dev(offsets, "offsets", (torch.int32,), 1)
+    groups, n2, k = bq.shape[0], bq.shape[1], bq.shape[2] * 2
+    if n2 % 2:
+        raise ValueError("b must have an even number of rows per expert (gate, then up)")
+    f = n2 // 2
+    if aq.shape[1] * 2 != k:
+        raise ValueError("A and B must have the same k")
+    if offsets.numel() != groups + 1:
+        raise ValueError("offsets must have groups + 1 entries")
+    a_rows = aq.shape[0]
+    m_total = _grouped_rows(a_rows, row_index, m_total)
+    dev = aq.device
+    _same_device(dev, ("b.q", bq), ("offsets", offsets), ("row_index", row_index))
+    if out is None:
+        h = torch.empty((m_total, f), dtype=torch.bfloat16, device=dev)
+        amax = torch.empty((m_total,), dtype=torch.float32, device=dev)
+    else:
+        h = _out_rows(out[0], "out.h", m_total, f, torch.bfloat16, dev)
+        amax = out[1]
+        _dev(amax, "out.amax", (torch.float32,), 1)
+        if amax.numel() < m_total or amax.device != dev:
+            raise ValueError("out.amax must have at least m_total entries on %s" % dev)
+    st = lib().nvfp4_grouped_gemm_swiglu(_ptr(aq), _ptr(asb), _ptr(as_), a_rows, _ptr(row_index),
+                                         m_total, _ptr(offsets), groups, _ptr(bq), _ptr(bsb),
+                                         _ptr(bs), f, k, _ptr(h), _ptr(amax), _stream(dev))
+    _check("nvfp4_grouped_gemm_swiglu", st)
+    return h, amax

@@ -43,6 +43,7 @@
 #include <type_traits>
 
 #include "gemm_common.h"
+#include "swiglu_core.h"
 
 namespace nvfp4 {
 
@@ -450,7 +451,7 @@ __device__ __forceinline__ void kstep(f32x16 (&acc)[4][4], lds_op_t<MX> (&fa)[4]
   for (int j = 0; j < 4; ++j) fb[j] = nb[j];
 }
 
-template <int VS, bool MX>
+template <int VS, bool MX, bool SW = false>
 __device__ __forceinline__ void lds_body(const GemmArgs& p, const LdsOperands& o, uint8_t* lds,
                                          int h, int li, int lane, int64_t row_lo, int64_t row_hi,
                                          int64_t n0, float rs0, float rs1) {
@@ -553,6 +554,47 @@ __device__ __forceinline__ void lds_body(const GemmArgs& p, const LdsOperands& o
 #pragma unroll
       for (int q = 0; q < 4; ++q)
         sc4[i][q] = *reinterpret_cast<const f32x4*>(s_rowscale + 32 * i + 8 * q + 4 * h);
+    if constexpr (SW) {
+      // SwiGLU epilogue: accumulator slabs 0-1 hold gate columns n0 + 32 j +
+      // li, slabs 2-3 the up columns of the same H columns.  g and u are the
+      // products the plain epilogue would store as Y; H[row, n0 + 32 j + li]
+      // = swiglu(g, u) as bf16.  Rows past the tile fall outside the store
+      // resource and columns past f get an out-of-range offset; each row's
+      // largest |h| over the tile's columns (a 32-lane maximum over li) goes
+      // to amax[row] by an atomic maximum of the bit pattern (order-free).
+      const int64_t f = p.n / 2;
+      const uint32_t hrow = (uint32_t)f * 2u;  // bytes per H row
+      const __amdgpu_buffer_rsrc_t rh =
+          out_rsrc(reinterpret_cast<float*>(p.h + row_lo * f), (row_hi - row_lo) * f * 2);
+      uint32_t vh[2];
+      bool cok[2];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        cok[j] = n0 + 32 * j + li < f;
+        vh[j] = cok[j] ? (uint32_t)(4 * h) * hrow + (uint32_t)(n0 + 32 * j + li) * 2u : 0x80000000u;
+      }
+#pragma unroll
+      for (int i = 0; i < VS; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            uint32_t m = 0;
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+              const float g = acc[i][j][4 * q + w] * sc4[i][q][w];
+              const float u = acc[i][j + 2][4 * q + w] * sc4[i][q][w];
+              const uint32_t b = swiglu_bf16(g, u);
+              __builtin_amdgcn_raw_buffer_store_b16((unsigned short)b, rh,
+                                                    vh[j] + (uint32_t)(32 * i + 8 * q + w) * hrow, 0, 2);
+              m = max(m, cok[j] ? (b & 0x7FFFu) : 0u);
+            }
+            m = group_max_u32<32>(m);
+            const int64_t row = row_lo + 32 * i + 8 * q + 4 * h + w;
+            if (li == 0 && row < row_hi) atomicMax(reinterpret_cast<unsigned int*>(p.amax + row), m << 16);
+          }
+      return;
+    }
     if ((p.n & 3) == 0) {
       // Through LDS, so every store writes 16 bytes and a store instruction
       // covers two whole 512-byte row segments: slab by slab, the scaled
@@ -640,9 +682,11 @@ __device__ __forceinline__ void lds_body(const GemmArgs& p, const LdsOperands& o
 // One 128 x 128 tile per one-wave block.  MX: operands are MXFP8 (E4M3
 // codes, one byte per element; E8M0 scales per 32) and there is no outer
 // scale (a_s, b_s unused).
-template <bool MX>
+template <bool MX, bool SW = false>
 __device__ __forceinline__ void lds_tile(const GemmArgs& p, uint8_t* s_lds) {
-  constexpr int BM = 128, BN = 128;
+  // SW: a tile is 64 columns of H, its B slabs the 64 gate rows (0-1) and
+  // the 64 up rows (2-3) of those columns
+  constexpr int BM = 128, BN = SW ? 64 : 128;
   static_assert(SCHED_LDS_WORDS * 4 <= LDS_CODES, "tile schedule must fit a code buffer");
   int32_t* s_prefix = reinterpret_cast<int32_t*>(s_lds + LDS_CODES);
 
@@ -673,6 +717,16 @@ __device__ __forceinline__ void lds_tile(const GemmArgs& p, uint8_t* s_lds) {
   // buffer range check turns into no read.
   const uint32_t OOB = 0x80000000u;
   const int cr = lane >> 2, cc = lane & 3;
+  // B row of row x of slab i, -1 past the weight (SW: gate rows n0 + 32 i + x
+  // for slabs 0-1, up rows f + n0 + 32 (i - 2) + x for slabs 2-3)
+  auto brow = [&](int i, int x) -> int64_t {
+    if (SW) {
+      const int64_t f = p.n / 2, c = n0 + 32 * (i & 1) + x;
+      return c < f ? (i >= 2 ? f + c : c) : -1;
+    }
+    const int64_t c = n0 + 32 * i + x;
+    return c < p.n ? c : -1;
+  };
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
 #pragma unroll
@@ -681,18 +735,18 @@ __device__ __forceinline__ void lds_tile(const GemmArgs& p, uint8_t* s_lds) {
       const uint32_t chunk = (uint32_t)((cc ^ lds_swz(lr)) * 16);
       const int64_t r = src_of(i >= 2, (32 * i + lr) & 63);
       o.aoff[i][u] = r >= 0 ? (uint32_t)(r * rowb) + chunk : OOB;
-      const int64_t c = n0 + 32 * i + lr;
-      o.boff[i][u] = c < p.n ? (uint32_t)(c * rowb) + chunk : OOB;
+      const int64_t c = brow(i, lr);
+      o.boff[i][u] = c >= 0 ? (uint32_t)(c * rowb) + chunk : OOB;
     }
     if (src_of(i >= 2, (32 * i + li) & 63) >= 0) o.avalid |= 1u << i;
-    if (n0 + 32 * i + li < p.n) o.bvalid |= 1u << i;
+    if (brow(i, li) >= 0) o.bvalid |= 1u << i;
   }
 #pragma unroll
   for (int q = 0; q < 2; ++q) {
     const int64_t r = q ? src1 : src0;
     o.asoff[q] = r >= 0 ? (uint32_t)(r * rows_s) : OOB;
-    const int64_t c = n0 + 64 * q + lane;
-    o.bsoff[q] = c < p.n ? (uint32_t)(c * rows_s) : OOB;
+    const int64_t c = brow(2 * q + (lane >> 5), lane & 31);
+    o.bsoff[q] = c >= 0 ? (uint32_t)(c * rows_s) : OOB;
   }
   // this lane's two epilogue row scales (rows lane and lane + 64), written to
   // LDS after the K loop
@@ -702,16 +756,21 @@ __device__ __forceinline__ void lds_tile(const GemmArgs& p, uint8_t* s_lds) {
   const float rs1 = MX ? 1.0f : (src1 >= 0 ? p.a_s[src1] : 0.0f) * sbw;
   const int vslabs = (int)min((int64_t)4, (row_hi - row_lo + 31) / 32);
   switch (vslabs) {
-    case 4: lds_body<4, MX>(p, o, s_lds, h, li, lane, row_lo, row_hi, n0, rs0, rs1); break;
-    case 3: lds_body<3, MX>(p, o, s_lds, h, li, lane, row_lo, row_hi, n0, rs0, rs1); break;
-    case 2: lds_body<2, MX>(p, o, s_lds, h, li, lane, row_lo, row_hi, n0, rs0, rs1); break;
-    default: lds_body<1, MX>(p, o, s_lds, h, li, lane, row_lo, row_hi, n0, rs0, rs1); break;
+    case 4: lds_body<4, MX, SW>(p, o, s_lds, h, li, lane, row_lo, row_hi, n0, rs0, rs1); break;
+    case 3: lds_body<3, MX, SW>(p, o, s_lds, h, li, lane, row_lo, row_hi, n0, rs0, rs1); break;
+    case 2: lds_body<2, MX, SW>(p, o, s_lds, h, li, lane, row_lo, row_hi, n0, rs0, rs1); break;
+    default: lds_body<1, MX, SW>(p, o, s_lds, h, li, lane, row_lo, row_hi, n0, rs0, rs1); break;
   }
 }
 
 __global__ __launch_bounds__(64) void gemm_lds_kernel(GemmArgs p) {
   __shared__ __attribute__((aligned(16))) uint8_t s_lds[lds_wave<false>()];
   lds_tile<false>(p, s_lds);
+}
+
+__global__ __launch_bounds__(64) void gemm_lds_swiglu_kernel(GemmArgs p) {
+  __shared__ __attribute__((aligned(16))) uint8_t s_lds[lds_wave<false>()];
+  lds_tile<false, true>(p, s_lds);
 }
 
 __global__ __launch_bounds__(64) void mxfp8_gemm_lds_kernel(GemmArgs p) {
@@ -822,5 +881,42 @@ extern "C" int nvfp4_grouped_gemm(const uint8_t* a_q, const uint8_t* a_sb, const
   // k == 0 needs no special case: the K loop is empty and the epilogue writes
   // zeros to exactly the rows the groups own
   if (!nvfp4::launch_gemm_skinny(p, true, str)) nvfp4::launch_gemm_rd<4, 4>(p, true, str);
+  return nvfp4host::launch_status();
+}
+
+extern "C" int nvfp4_grouped_gemm_swiglu(const uint8_t* a_q, const uint8_t* a_sb, const float* a_s,
+                                         int64_t a_rows, const int32_t* row_index, int64_t m_total,
+                                         const int32_t* offsets, int64_t groups, const uint8_t* b_q,
+                                         const uint8_t* b_sb, const float* b_s, int64_t f, int64_t k,
+                                         uint16_t* h, float* amax, void* stream) {
+  if (groups < 1 || a_rows < 0 || m_total < 0 || f < 0 || k < 0) return NVFP4_ERROR_INVALID_VALUE;
+  if (k == 0 || k % 256 != 0 || groups > nvfp4::MAX_GROUPS) return NVFP4_ERROR_UNSUPPORTED_SHAPE;
+  if (m_total == 0 || f == 0) return NVFP4_SUCCESS;
+  if (!offsets || !h || !amax || !b_s || !b_q || !b_sb) return NVFP4_ERROR_INVALID_VALUE;
+  if (a_rows > 0 && (!a_q || !a_sb || !a_s)) return NVFP4_ERROR_INVALID_VALUE;
+  if (!row_index && a_rows < m_total) return NVFP4_ERROR_INVALID_VALUE;
+  const int64_t lim = (int64_t)1 << 31;
+  if (m_total > lim || a_rows > lim || 2 * f >= ((int64_t)1 << 22) || k > ((int64_t)1 << 24) ||
+      a_rows * (k / 2) >= lim || 2 * f * (k / 2) >= lim)
+    return NVFP4_ERROR_UNSUPPORTED_SHAPE;
+  if (!aligned(a_q, 16) || !aligned(b_q, 16) || !aligned(a_sb, 16) || !aligned(b_sb, 16) ||
+      !aligned(a_s, 4) || !aligned(b_s, 4) || !aligned(offsets, 4) || !aligned(row_index, 4) ||
+      !aligned(h, 2) || !aligned(amax, 4))
+    return NVFP4_ERROR_MISALIGNED;
+  int st = nvfp4host::check_arch();
+  if (st) return st;
+  hipStream_t str = (hipStream_t)stream;
+  // the row maxima are atomic maxima over the column tiles: start from zero
+  // (a fill kernel, so the sequence can be captured in a graph)
+  const int64_t zb = (m_total + 255) / 256;
+  hipLaunchKernelGGL(nvfp4::zero_rows_kernel, dim3((unsigned)(zb < 1024 ? zb : 1024)), dim3(256), 0,
+                     str, amax, m_total);
+  nvfp4::GemmArgs p{};
+  p.a_q = a_q; p.a_sb = a_sb; p.a_s = a_s; p.a_rows = a_rows;
+  p.row_index = row_index; p.t.m_total = m_total; p.t.offsets = offsets; p.t.groups = (int)groups;
+  p.b_q = b_q; p.b_sb = b_sb; p.b_s = b_s; p.n = 2 * f; p.k = k; p.y = nullptr;
+  p.h = h; p.amax = amax;
+  const int64_t blocks = nvfp4::plan_tiles<128, 64>(p.t, f, true);
+  hipLaunchKernelGGL(nvfp4::gemm_lds_swiglu_kernel, dim3((unsigned)blocks), dim3(64), 0, str, p);
   return nvfp4host::launch_status();
 }

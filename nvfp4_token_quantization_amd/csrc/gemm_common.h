@@ -18,6 +18,10 @@ struct GemmArgs {
   int64_t n, k;
   float* y;
   TileGrid t;  // output rows / expert offsets and the launch plan
+  // SwiGLU epilogue only (else null): bf16 H [m_total, n / 2] and its row
+  // amax [m_total] (atomic maxima of the bit patterns; zeroed beforehand)
+  uint16_t* h;
+  float* amax;
 };
 
 __device__ __forceinline__ f16x2 as_h2(uint32_t v) { return __builtin_bit_cast(f16x2, v); }
