@@ -60,6 +60,26 @@ def test_grouped_1024_groups():
     assert np.all(np.isnan(y[m_total:])), "rows past offsets[groups] must not be written"
 
 
+def test_grouped_1024_groups_tiled_kernel():
+    """The same expert pattern with every count times 4 (more than 16 rows per
+    expert on average): the tiled kernel's schedule, whose expert prefix
+    reads the offsets in 64-expert segments, over all 1024 experts."""
+    counts = 4 * _counts_1024(504)
+    groups, n, k, tokens = 1024, 64, 256, 501
+    assert counts.sum() > 16 * groups
+    x = sg.student_t3_bf16(505, 1, (tokens, k))
+    a = oracle.quantize_rows(x)
+    w = sg.normal_bf16(506, 2, (groups, n, k), 0.0, 0.02)
+    b = oracle.quantize_weight(w)[:3]
+    offsets = np.zeros(groups + 1, np.int32)
+    offsets[1:] = np.cumsum(counts)
+    m_total = int(offsets[-1])
+    ri = ((np.arange(m_total) * 7919) % tokens).astype(np.int32)
+    y = to_np(nv.nvfp4_grouped_gemm(dev_op(a), to_dev(offsets), dev_op(b), row_index=to_dev(ri)))
+    y_ref, bound = oracle.grouped_gemm(a, offsets, b, row_index=ri)
+    check_gemm(y, y_ref, bound, "1024 groups, tiled, %d rows" % m_total)
+
+
 def test_mxfp8_grouped_1024_groups():
     from test_gpu_mxfp8 import check_mx_gemm, grouped_reference
     counts = _counts_1024(511)
