@@ -94,22 +94,19 @@ __device__ __forceinline__ int find_expert(const int32_t* s_prefix, int G, int m
   return count - 1;
 }
 
-// A readable int32 for the gathered-row load below when there is no index
-// (its value is never used).
-__device__ int32_t k_no_row_index[1] = {0};
-
 // The A row that output row `out_row` of a tile with rows [.., row_hi)
 // reads: row_index[out_row] (or out_row itself without an index), -1 when
 // the output row is past the tile or the index falls outside [0, a_rows).
-// The index load is unconditional and branch-free (clamped to the tile's
-// last row, which exists; a dummy word without an index), so the loads of a
-// lane's rows go out together instead of each waiting behind a branch.
+// With an index the load is unconditional (clamped to the tile's last row,
+// which exists), so the loads of a lane's rows go out together instead of
+// each waiting behind a per-lane branch.
 __device__ __forceinline__ int64_t gathered_row(const int32_t* row_index, int64_t a_rows,
                                                 int64_t out_row, int64_t row_hi) {
+  // without an index (a kernel argument, so the branch is uniform) there is
+  // nothing to load: the A row is the output row
+  if (!row_index) return (out_row < row_hi && out_row < a_rows) ? out_row : -1;
   const int64_t rr = min(out_row, row_hi - 1);
-  const int32_t* src = row_index ? row_index + rr : k_no_row_index;
-  const int32_t v = *src;
-  const int64_t r = row_index ? (int64_t)v : rr;
+  const int64_t r = (int64_t)row_index[rr];
   return (out_row < row_hi && r >= 0 && r < a_rows) ? r : -1;
 }
 
