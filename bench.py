@@ -61,7 +61,7 @@ T0 = time.time()
 
 # Source files each timed kernel is built from (its traffic counters stay
 # valid until one of these changes).
-_QUANT_SRC = ("quantize.hip", "nvfp4_internal.h", "host_util.hip")
+_QUANT_SRC = ("quantize.hip", "quant_rows.h", "weight_onepass.h", "nvfp4_internal.h", "host_util.hip")
 _GEMM_SRC = ("gemm.hip", "gemm_common.h", "tile_sched.h", "nvfp4_internal.h", "host_util.hip")
 _SKINNY_SRC = ("gemm_skinny.hip", "gemm_common.h", "tile_sched.h", "nvfp4_internal.h", "host_util.hip")
 KERNEL_SOURCES = {
@@ -97,10 +97,11 @@ def quant_rows_bytes(rows, k, amax_in=False):
 
 
 def quant_weight_bytes(groups, rows, k):
-    # the group amax must be known before any element is encoded, so the
-    # bf16 weight is read twice (amax pass, encode pass)
+    # the least any implementation moves: the bf16 weight read once, the
+    # codes, block scales and per-group scales written (the one-pass kernel
+    # moves just this; the two-pass form reads the weight a second time)
     n = groups * rows * k
-    return 2 * n * 2 + n // 2 + n // 16 + groups * 4
+    return n * 2 + n // 2 + n // 16 + groups * 4
 
 
 def gemm_bytes(a_rows, m_out, n, k, groups):

@@ -109,6 +109,12 @@ int nvfp4_quantize_rows(const uint16_t* x_bf16, int64_t rows, int64_t k, const f
  * Each row is encoded exactly as nvfp4_quantize_rows would encode it with
  * amax_in set to its group's amax.  Errors as for nvfp4_quantize_rows, plus
  * INVALID_VALUE for groups < 1 or a missing amax_out.
+ * When the amax is computed here and there are at least 8 groups of at
+ * least 512 KiB of bf16, the weight is read once: while the call runs,
+ * amax_out[g] holds the partial maximum and s[g] a count of the workgroups
+ * that share group g (both final when the call's work completes).  amax_out
+ * and s must not overlap each other or the other buffers (overlapping
+ * amax_out and s take the two-pass form).  No workspace is allocated.
  */
 int nvfp4_quantize_weight(const uint16_t* w_bf16, int64_t groups, int64_t rows_per_group,
                           int64_t k, const float* amax_in, float* amax_out, uint8_t* q,

@@ -16,8 +16,9 @@ extern "C" {
 #endif
 
 /*
- * Codec self-test hooks: apply the device rounding functions the quantizer
- * uses to arbitrary fp32 inputs, so tests can sweep every bit pattern.
+ * Self-test hooks: apply the device rounding functions the quantizer uses to
+ * arbitrary fp32 inputs, so tests can sweep every bit pattern; and run the
+ * one-pass weight quantizer on shapes and time limits of a test's choosing.
  *   nvfp4_debug_encode_e2m1: code[i] = 4-bit E2M1 code (sign | RNE_SAT
  *     magnitude) of v[i]; +-inf saturate; NaN inputs give unspecified codes.
  *   nvfp4_debug_encode_e4m3: code[i] = RNE_SAT E4M3 code of v[i] >= 0
@@ -40,6 +41,16 @@ int nvfp4_debug_encode_e4m3(const float* v, int64_t n, uint8_t* code, void* stre
  * all device memory.  amax[i] must be finite and >= 0.  Errors as above. */
 int nvfp4_debug_block_scale(const uint16_t* block_amax, const float* amax, int64_t n,
                             uint8_t* code, float* inv, void* stream);
+/* nvfp4_debug_quantize_weight_onepass: nvfp4_quantize_weight (amax_in NULL)
+ * forced onto its one-pass kernel, at any group size, with each workgroup's
+ * wait for its team bounded by limit_ms milliseconds (0: a workgroup that
+ * does not find every member arrived at once takes the group amax by reading
+ * the whole group itself).  Arguments and outputs as nvfp4_quantize_weight;
+ * amax_out and s must not overlap.  UNSUPPORTED_SHAPE when the one-pass
+ * kernel cannot hold a group (the library then uses two passes). */
+int nvfp4_debug_quantize_weight_onepass(const uint16_t* w_bf16, int64_t groups, int64_t rows_per_group,
+                                        int64_t k, float* amax_out, uint8_t* q, uint8_t* sb, float* s,
+                                        double limit_ms, void* stream);
 
 #ifdef __cplusplus
 }

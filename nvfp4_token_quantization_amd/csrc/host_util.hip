@@ -1,6 +1,6 @@
 // host_util.hip -- host-side helpers shared by libnvfp4.so and the codec
-// self-test library: the gfx950 check and CU count per device (cached), and
-// the launch status.
+// self-test library: the gfx950 check, CU count and wall-clock rate per
+// device (cached), and the launch status.
 #include <string.h>
 
 #include "nvfp4_internal.h"
@@ -31,6 +31,19 @@ int num_cus() {
   if (v == 0) {
     if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0)
       v = 256;
+    __atomic_store_n(&cache[dev], v, __ATOMIC_RELEASE);
+  }
+  return v;
+}
+
+int64_t wall_clock_khz() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 100000;
+  int v = __atomic_load_n(&cache[dev], __ATOMIC_ACQUIRE);
+  if (v == 0) {
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeWallClockRate, dev) != hipSuccess || v <= 0)
+      v = 100000;
     __atomic_store_n(&cache[dev], v, __ATOMIC_RELEASE);
   }
   return v;

@@ -212,6 +212,10 @@ int check_arch();
 // Compute units of the current device (cached per device).
 int num_cus();
 
+// Rate of the device's constant wall clock (wall_clock64) in kHz (cached per
+// device).
+int64_t wall_clock_khz();
+
 // Maps the last HIP launch error to a status.
 int launch_status();
 

@@ -1,8 +1,10 @@
-// selftest.hip -- libnvfp4_selftest.so: codec self-test hooks that apply the
-// device rounding functions of the quantizers to arbitrary fp32 inputs, so
-// tests can sweep every bit pattern.  Test-only: not part of libnvfp4.so or
-// of its header; declared in include/nvfp4_selftest.h.
+// selftest.hip -- libnvfp4_selftest.so: self-test hooks that apply the device
+// rounding functions of the quantizers to arbitrary fp32 inputs, so tests can
+// sweep every bit pattern, and run the one-pass weight quantizer on any group
+// size with a chosen bound on its wait.  Test-only: not part of libnvfp4.so
+// or of its header; declared in include/nvfp4_selftest.h.
 #include "mxfp8_codec.h"
+#include "weight_onepass.h"
 #include "nvfp4_selftest.h"
 
 namespace nvfp4 {
@@ -94,6 +96,25 @@ int nvfp4_debug_encode_fp8(const float* v, int64_t n, uint8_t* code, void* strea
   const int64_t need = (n + 255) / 256;
   dim3 grid((unsigned)(need < 4096 ? need : 4096));
   hipLaunchKernelGGL(nvfp4::debug_fp8_kernel, grid, dim3(256), 0, (hipStream_t)stream, v, n, code);
+  return nvfp4host::launch_status();
+}
+
+int nvfp4_debug_quantize_weight_onepass(const uint16_t* w, int64_t groups, int64_t rows_per_group,
+                                        int64_t k, float* amax_out, uint8_t* q, uint8_t* sb, float* s,
+                                        double limit_ms, void* stream) {
+  if (groups < 1 || rows_per_group < 1 || k < 16 || !(limit_ms >= 0.0)) return NVFP4_ERROR_INVALID_VALUE;
+  if (k % 16 != 0) return NVFP4_ERROR_UNSUPPORTED_SHAPE;
+  if (!w || !amax_out || !q || !sb || !s) return NVFP4_ERROR_INVALID_VALUE;
+  if (groups * rows_per_group > ((int64_t)1 << 36) || k > ((int64_t)1 << 30))
+    return NVFP4_ERROR_UNSUPPORTED_SHAPE;
+  if (!nvfp4host::aligned(w, 16) || !nvfp4host::aligned(q, 16) || !nvfp4host::aligned(s, 4) ||
+      !nvfp4host::aligned(amax_out, 4))
+    return NVFP4_ERROR_MISALIGNED;
+  int st = nvfp4host::check_arch();
+  if (st) return st;
+  if (!nvfp4::launch_weight_onepass(w, groups, rows_per_group, k, amax_out, q, sb, s, limit_ms, 0, 1,
+                                    (hipStream_t)stream))
+    return NVFP4_ERROR_UNSUPPORTED_SHAPE;
   return nvfp4host::launch_status();
 }
 

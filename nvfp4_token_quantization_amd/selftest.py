@@ -1,7 +1,8 @@
-"""Codec self-test hooks (test-only) over ``libnvfp4_selftest.so``, declared
-in ``include/nvfp4_selftest.h``: the quantizers' device rounding functions
-applied to arbitrary float32 inputs, so tests can sweep every bit pattern.
-Not part of the product boundary; raises if the library is not built."""
+"""Self-test hooks (test-only) over ``libnvfp4_selftest.so``, declared in
+``include/nvfp4_selftest.h``: the quantizers' device rounding functions
+applied to arbitrary float32 inputs, so tests can sweep every bit pattern, and
+the one-pass weight quantizer on any group size with a chosen bound on its
+wait.  Not part of the product boundary; raises if the library is not built."""
 import ctypes
 import os
 
@@ -25,6 +26,8 @@ def lib():
             getattr(L, f).restype = ctypes.c_int
         L.nvfp4_debug_block_scale.argtypes = [P, P, I64, P, P, P]
         L.nvfp4_debug_block_scale.restype = ctypes.c_int
+        L.nvfp4_debug_quantize_weight_onepass.argtypes = [P, I64, I64, I64, P, P, P, P, ctypes.c_double, P]
+        L.nvfp4_debug_quantize_weight_onepass.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -71,3 +74,23 @@ def nvfp4_debug_encode_fp8(v):
     nv._check("nvfp4_debug_encode_fp8",
            lib().nvfp4_debug_encode_fp8(nv._ptr(v), v.numel(), nv._ptr(out), nv._stream(v.device)))
     return out
+
+
+def nvfp4_debug_quantize_weight_onepass(w, limit_ms=10.0):
+    """nvfp4_quantize_weight of a bf16 [groups, rows, k] weight (group amax
+    computed) forced onto the one-pass kernel, each workgroup's wait for its
+    team bounded by limit_ms (0: workgroups that do not find the team complete
+    read the whole group themselves).  Returns (q, sb, s, amax) shaped as
+    nvfp4_quantize_weight's; raises NVFP4Error (UNSUPPORTED_SHAPE) when the
+    kernel cannot hold a group."""
+    nv._dev(w, "w", nv._BF16, 3)
+    groups, rows, k = w.shape
+    d = w.device
+    q = torch.empty((groups, rows, k // 2), dtype=torch.uint8, device=d)
+    sb = torch.empty((groups, rows, k // 16), dtype=torch.uint8, device=d)
+    s = torch.empty(groups, dtype=torch.float32, device=d)
+    amax = torch.empty(groups, dtype=torch.float32, device=d)
+    nv._check("nvfp4_debug_quantize_weight_onepass",
+              lib().nvfp4_debug_quantize_weight_onepass(nv._ptr(w), groups, rows, k, nv._ptr(amax), nv._ptr(q),
+                                                        nv._ptr(sb), nv._ptr(s), float(limit_ms), nv._stream(d)))
+    return q, sb, s, amax

@@ -52,7 +52,8 @@ def test_library_exports_every_declared_symbol(L):
 def test_selftest_hooks_live_outside_the_product_library(L, S):
     hooks = declared_functions(SELFTEST_HEADER)
     assert sorted(hooks) == ["nvfp4_debug_block_scale", "nvfp4_debug_encode_e2m1",
-                             "nvfp4_debug_encode_e4m3", "nvfp4_debug_encode_fp8"]
+                             "nvfp4_debug_encode_e4m3", "nvfp4_debug_encode_fp8",
+                             "nvfp4_debug_quantize_weight_onepass"]
     assert not set(hooks) & set(declared_functions())
     for name in hooks:
         assert hasattr(S, name), name
@@ -100,6 +101,18 @@ def test_quantize_weight_argument_errors(L):
     assert f(a, 2, 4, 16, None, a, a, a, None, None) == INVALID     # no s
     assert f(None, 2, 4, 16, None, a, a, a, a, None) == INVALID
     assert f(P(FAKE_ODD), 2, 4, 16, None, a, a, a, a, None) == MISALIGNED
+
+
+def test_onepass_hook_argument_errors(S):
+    f = S.nvfp4_debug_quantize_weight_onepass
+    a, ms = P(FAKE), ctypes.c_double(10.0)
+    assert f(a, 0, 4, 16, a, a, a, a, ms, None) == INVALID                     # zero groups
+    assert f(a, 2, 0, 16, a, a, a, a, ms, None) == INVALID                     # no rows
+    assert f(a, 2, 4, 16, a, a, a, a, ctypes.c_double(-1.0), None) == INVALID  # negative limit
+    assert f(a, 2, 4, 40, a, a, a, a, ms, None) == SHAPE
+    assert f(a, 2, 4, 16, None, a, a, a, ms, None) == INVALID                  # no amax target
+    assert f(a, 2, 4, 16, a, a, a, None, ms, None) == INVALID                  # no s
+    assert f(P(FAKE_ODD), 2, 4, 16, a, a, a, a, ms, None) == MISALIGNED
 
 
 def test_gemm_argument_errors(L):
