@@ -111,10 +111,11 @@ int nvfp4_quantize_rows(const uint16_t* x_bf16, int64_t rows, int64_t k, const f
  * INVALID_VALUE for groups < 1 or a missing amax_out.
  * When the amax is computed here and there are at least 8 groups of at
  * least 512 KiB of bf16, the weight is read once: while the call runs,
- * amax_out[g] holds the partial maximum and s[g] a count of the workgroups
- * that share group g (both final when the call's work completes).  amax_out
- * and s must not overlap each other or the other buffers (overlapping
- * amax_out and s take the two-pass form).  No workspace is allocated.
+ * amax_out[g], s[g] and the first 256 bytes of group g's codes in q hold the
+ * partial maxima and counts of the workgroups that share group g (all hold
+ * their final values when the call's work completes).  amax_out, s and q
+ * must not overlap each other or the other buffers (overlapping amax_out and
+ * s take the two-pass form).  No workspace is allocated.
  */
 int nvfp4_quantize_weight(const uint16_t* w_bf16, int64_t groups, int64_t rows_per_group,
                           int64_t k, const float* amax_in, float* amax_out, uint8_t* q,

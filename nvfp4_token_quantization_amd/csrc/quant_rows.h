@@ -84,13 +84,15 @@ __device__ __forceinline__ uint32_t pair_max(uint32_t v) {
 }
 
 // Encode and store one row group.  Must be called by all 64 lanes of the
-// wave (block and row amax are cross-lane reductions).
+// wave (block and row amax are cross-lane reductions).  The first `qskip`
+// code dwords of the row are left unwritten (a caller writes them later).
 template <int L, int U, int MODE>
 __device__ __forceinline__ void encode_rows(const RowData<U>& r, int64_t rows, int64_t k, int nh,
                                             int64_t row, int j,
                                             const float* __restrict__ amax_src,
                                             int64_t rows_per_group, uint8_t* __restrict__ q,
-                                            uint8_t* __restrict__ sb, float* __restrict__ s) {
+                                            uint8_t* __restrict__ sb, float* __restrict__ s,
+                                            int qskip = 0) {
   const bool row_ok = row < rows;
   uint32_t bmax[U];
   uint32_t rmax = 0;
@@ -130,7 +132,7 @@ __device__ __forceinline__ void encode_rows(const RowData<U>& r, int64_t rows, i
   for (int i = 0; i < U; ++i) {
     const int h = j + L * i;
     if (row_ok && h < nh) {
-      qr[h] = encode_half(r.d[i], inv[i]);
+      if (h >= qskip) qr[h] = encode_half(r.d[i], inv[i]);
       if (!odd) sr[h >> 1] = (uint8_t)code[i];
     }
   }

@@ -9,7 +9,8 @@ Every output must equal the oracle's quantize_weight bit for bit:
   groups (rows not a multiple of the rows per row group), group counts that
   do not fill the last round of teams, an all-zero group and a group holding
   the largest finite bf16, every lanes-per-row layout (16, 32 and 64 lanes,
-  1 to 8 half-blocks per lane);
+  1 to 8 half-blocks per lane), and slot areas (the first 64 code dwords of
+  a group, written last) that span several rows or end inside one;
 - the self-test hook with a zero time limit, where workgroups that do not
   find their team complete read the whole group themselves;
 - the hook on small groups and few groups (below the library's thresholds,
@@ -42,6 +43,8 @@ def weight(seed, groups, rows, k, std=0.02):
     (8, 200, 4096),    # 64 x 8
     (9, 1000, 592),    # 16 x 5, a row's last lanes idle
     (12, 130, 2048),   # 64 x 4
+    (16, 16384, 16),   # 16 x 1, two rounds: a slot area spans 32 rows
+    (32, 6000, 48),    # 16 x 1, two rounds: a slot area ends inside a row
 ])
 def test_onepass_product_path_matches_oracle(groups, rows, k):
     # groups of at least 512 KiB and at least 8 of them (one team per XCD)
