@@ -112,8 +112,11 @@ def gemm_bytes(a_rows, m_out, n, k, groups):
 
 # Launch order of one step and the number of kernel dispatches each makes
 # (a weight quantize is: clear amax target, group amax, encode with scales).
-STEP_LAUNCHES = [("quantize_weight_dense", 3), ("quantize_weight_up", 3),
-                 ("quantize_weight_down", 3), ("quantize_rows_dense", 1), ("quantize_rows_moe", 1),
+# dispatches per launch of the step, in order: the dense W (one group) takes
+# the two passes (clear, amax, encode); W_up and W_dn the one-pass kernel
+# after its clear
+STEP_LAUNCHES = [("quantize_weight_dense", 3), ("quantize_weight_up", 2),
+                 ("quantize_weight_down", 2), ("quantize_rows_dense", 1), ("quantize_rows_moe", 1),
                  ("gemm_dense", 1), ("grouped_gemm_up", 1), ("requantize_rows_amax_reuse", 1),
                  ("grouped_gemm_down", 1)]
 CALIB_BYTES = 1 << 30
