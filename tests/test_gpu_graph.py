@@ -10,8 +10,9 @@ import pytest
 import torch
 
 import nvfp4_token_quantization_amd as nv
+import oracle
 import synthgen as sg
-from gpu_helpers import dev, to_dev
+from gpu_helpers import assert_same_quant, dev, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -81,3 +82,41 @@ def test_graph_replays_match_eager():
                 bad = int((got != w).sum())
                 raise AssertionError("replay %d: output %d differs from eager in %d entries" % (
                     rep, name, bad))
+
+
+def test_graph_replays_one_pass_weight_quantize():
+    """The one-pass weight quantizer (its clear kernel, then the team kernel
+    with a slot round and an atomic round per team: 32 groups of 4096 x 256)
+    recorded in a graph: every replay, with a different weight quantized
+    eagerly in between on the same kind of buffers, equals the eager result
+    and the oracle."""
+    G, R, K = 32, 4096, 256
+    assert R * K * 2 >= 512 * 1024 and G >= 8
+    w = sg.normal_bf16(95, sg.S_W, (G, R, K), 0.0, 0.02)
+    wd, w2 = to_dev(w), to_dev(sg.normal_bf16(96, sg.S_W, (G, R, K), 0.0, 0.05))
+    want = oracle.quantize_weight(w)
+
+    def alloc():
+        d = dev()
+        return (torch.empty((G, R, K // 2), dtype=torch.uint8, device=d),
+                torch.empty((G, R, K // 16), dtype=torch.uint8, device=d),
+                torch.empty((G,), dtype=torch.float32, device=d), torch.empty((G,), dtype=torch.float32, device=d))
+
+    outs = alloc()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        nv.nvfp4_quantize_weight(wd, out=outs)  # warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        nv.nvfp4_quantize_weight(wd, out=outs)
+    other = alloc()
+    for rep in range(4):
+        for t in outs:
+            t.fill_(77 if t.dtype == torch.uint8 else 3.0)  # stale values in the slot and counter words
+        g.replay()
+        nv.nvfp4_quantize_weight(w2, out=other)  # eager work between replays
+        torch.cuda.synchronize()
+        assert_same_quant(outs, want, "replay %d" % rep)
