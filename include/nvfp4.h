@@ -115,7 +115,10 @@ int nvfp4_quantize_rows(const uint16_t* x_bf16, int64_t rows, int64_t k, const f
  * partial maxima and counts of the workgroups that share group g (all hold
  * their final values when the call's work completes).  amax_out, s and q
  * must not overlap each other or the other buffers (overlapping amax_out and
- * s take the two-pass form).  No workspace is allocated.
+ * s take the two-pass form).  No workspace is allocated.  Work on other
+ * streams may hold CUs that the call's workgroups wait for: a workgroup
+ * waits at most 10 ms for its team before reading the group itself for its
+ * amax, so the results are exact in every case.
  */
 int nvfp4_quantize_weight(const uint16_t* w_bf16, int64_t groups, int64_t rows_per_group,
                           int64_t k, const float* amax_in, float* amax_out, uint8_t* q,

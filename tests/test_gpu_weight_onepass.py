@@ -104,3 +104,27 @@ def test_onepass_hook_rejects_rows_it_cannot_hold():
     q, sb, s, amax = nv.nvfp4_quantize_weight(w)
     assert float(s[0]) == 0.0 and float(amax[0]) == 0.0
     assert int(q.sum()) == 0 and int(sb.sum()) == 0
+
+
+def test_onepass_concurrent_streams():
+    """Two one-pass quantizations launched back to back on two streams (32
+    groups of 2048 x 512 each: a slot round and an atomic round per team)
+    compete for the CUs, so a team's members need not all be resident at
+    once; whatever each member's wait does (the team completes, or its time
+    limit sends it down the read-the-group path), both results equal the
+    oracle's."""
+    G, R, K = 32, 2048, 512
+    w1 = weight(501, G, R, K)
+    w2 = weight(502, G, R, K, std=0.05)
+    want1, want2 = oracle.quantize_weight(w1), oracle.quantize_weight(w2)
+    d1, d2 = to_dev(w1), to_dev(w2)
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        with torch.cuda.stream(s1):
+            got1 = nv.nvfp4_quantize_weight(d1)
+        with torch.cuda.stream(s2):
+            got2 = nv.nvfp4_quantize_weight(d2)
+        torch.cuda.synchronize()
+        assert_same_quant(got1, want1, "stream 1, repeat %d" % rep)
+        assert_same_quant(got2, want2, "stream 2, repeat %d" % rep)
