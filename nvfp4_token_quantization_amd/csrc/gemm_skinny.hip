@@ -10,7 +10,7 @@
 // differs is how the work is split, because a 128 x 128 output tile per wave
 // leaves most of the chip idle when M is 64:
 //  - a workgroup owns one item: dense, up to 64 rows by 48 columns, K split
-//    over up to 10 waves, each taking a contiguous run of 256-element chunks
+//    over up to 8 waves, each taking a contiguous run of 256-element chunks
 //    (two 128-element pieces; K % 256 == 0); grouped, up to 32 rows of one
 //    expert by 48 columns, K split over up to 3 waves;
 //  - a chunk's operand bytes reach the wave's private LDS by DMA
@@ -364,13 +364,14 @@ bool launch_gemm_skinny(const GemmArgs& a, bool grouped, hipStream_t stream) {
   void (*k)(SkinnyArgs);
   if (!grouped) {
     // one workgroup per item of 64 rows x 48 columns (N = 9728: 203 items,
-    // one round on 256 CUs), K split over up to 10 waves (one chunk each at
-    // K = 2560) and the partial tiles summed in LDS
+    // one round on 256 CUs), K split over up to 8 waves (one or two chunks
+    // each at K = 2560; measured 12.1 us against 12.8 with 10 waves, 12.4
+    // with 7, 13.3 with 9) and the partial tiles summed in LDS
     p.bm = 64;
     p.nblocks = (int)((a.n + 47) / 48);
     p.items = p.nblocks;
-    p.ks = (int)min((int64_t)10, p.pieces / SK_NT);
-    k = gemm_skinny_kernel<4, 3, 10, 1, false>;
+    p.ks = (int)min((int64_t)8, p.pieces / SK_NT);
+    k = gemm_skinny_kernel<4, 3, 8, 1, false>;
     grid = p.items;
   } else {
     // items of up to 32 rows of one expert (decode experts mostly hold at

@@ -4,7 +4,7 @@ compared.  The library takes this path for a dense M of at most 64, or at most
 16 routed rows per expert on average, when K is a multiple of 256.  Dense
 items are 64 rows x 48 columns with K split over the waves of a workgroup and
 the partial tiles summed in a fixed order, so the path is checked for several
-K splits (1 to 10 waves, even and uneven); grouped items are up to 32 rows
+K splits (1 to 8 waves, even and uneven); grouped items are up to 32 rows
 of one expert x 48 columns with K split over up to 3 waves.  Also covered: ragged rows and columns, experts longer
 than one item, empty experts, gathered rows, invalid row indices and
 bit-identical repeated results.
@@ -32,9 +32,10 @@ def operands(seed, m, n, k, groups=1):
 
 
 # The path takes K % 256 == 0 (whole chunks of 256 elements) and, dense,
-# splits the chunks over up to 10 waves: 256 -> one wave; 512 ->
-# two; 768 -> three; 1280 -> five; 2048 -> eight; 2560 -> ten; 16384 -> ten
-# waves of 6 or 7 chunks.  K = 640 and 64 take the tiled kernels instead.
+# splits the chunks over up to 8 waves: 256 -> one wave; 512 -> two; 768 ->
+# three; 1280 -> five; 2048 -> eight; 2560 -> eight waves of 2, 2 and six of
+# 1 chunk; 16384 -> eight waves of 8 chunks.  K = 640 and 64 take the tiled
+# kernels instead.
 @pytest.mark.parametrize("m,n,k", [(1, 1, 256), (1, 96, 768), (17, 200, 768), (32, 64, 2560),
                                    (33, 130, 2560), (64, 9728, 2560), (64, 1536, 2048),
                                    (5, 300, 16384), (64, 33, 512), (48, 1000, 1280),
