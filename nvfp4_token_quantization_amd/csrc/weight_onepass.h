@@ -362,6 +362,7 @@ static bool launch_weight_onepass(const uint16_t* w, int64_t groups, int64_t R, 
                                   uint8_t* q, uint8_t* sb, float* s, double limit_ms,
                                   int64_t min_group_bytes, int min_teams, hipStream_t stream) {
   if (groups < 1 || R < 1 || k < 16 || groups >= ((int64_t)1 << 31)) return false;
+  if (R > (((int64_t)1 << 40) / k)) return false;  // a group's bytes stay far from overflow
   if (R * k * 2 < min_group_bytes) return false;
   // the counter lives in s and the maximum in amax_out: they must be distinct
   if (amax_out + groups > s && s + groups > amax_out) return false;
