@@ -108,14 +108,15 @@ int nvfp4_quantize_rows(const uint16_t* x_bf16, int64_t rows, int64_t k, const f
  *   out; s [groups] f32 out (S per group).
  * Each row is encoded exactly as nvfp4_quantize_rows would encode it with
  * amax_in set to its group's amax.  Errors as for nvfp4_quantize_rows, plus
- * INVALID_VALUE for groups < 1 or a missing amax_out.
+ * INVALID_VALUE for groups < 1, a missing amax_out, or amax_out and s
+ * overlapping.
  * When the amax is computed here and there are at least 8 groups of at
  * least 512 KiB of bf16, the weight is read once: while the call runs,
  * amax_out[g], s[g] and the first 256 bytes of group g's codes in q hold the
  * partial maxima and counts of the workgroups that share group g (all hold
  * their final values when the call's work completes).  amax_out, s and q
- * must not overlap each other or the other buffers (overlapping amax_out and
- * s take the two-pass form).  No workspace is allocated.  Work on other
+ * must not overlap each other or the other buffers.  No workspace is
+ * allocated.  Work on other
  * streams may hold CUs that the call's workgroups wait for: a workgroup
  * waits at most 10 ms for its team before reading the group itself for its
  * amax, so the results are exact in every case.

@@ -283,6 +283,8 @@ extern "C" int nvfp4_quantize_weight(const uint16_t* w_bf16, int64_t groups, int
   if (!aligned(w_bf16, 16) || !aligned(q, 16) || !aligned(s, 4) || !aligned(amax_in, 4) ||
       !aligned(amax_out, 4))
     return NVFP4_ERROR_MISALIGNED;
+  // amax_out is written while s is (the reduction target, then the scales)
+  if (amax_out && amax_out < s + groups && s < amax_out + groups) return NVFP4_ERROR_INVALID_VALUE;
   int st = nvfp4host::check_arch();
   if (st) return st;
   hipStream_t str = (hipStream_t)stream;

@@ -101,6 +101,9 @@ def test_quantize_weight_argument_errors(L):
     assert f(a, 2, 4, 16, None, a, a, a, None, None) == INVALID     # no s
     assert f(None, 2, 4, 16, None, a, a, a, a, None) == INVALID
     assert f(P(FAKE_ODD), 2, 4, 16, None, a, a, a, a, None) == MISALIGNED
+    # amax_out and s overlapping (the same array, or shifted by one entry)
+    assert f(a, 2, 4, 16, None, a, a, a, a, None) == INVALID
+    assert f(a, 2, 4, 16, None, P(FAKE + 4), a, a, a, None) == INVALID
 
 
 def test_onepass_hook_argument_errors(S):
