@@ -128,3 +128,25 @@ def test_onepass_concurrent_streams():
         torch.cuda.synchronize()
         assert_same_quant(got1, want1, "stream 1, repeat %d" % rep)
         assert_same_quant(got2, want2, "stream 2, repeat %d" % rep)
+
+
+def test_onepass_hook_random_shapes():
+    """A seeded sweep of shapes through the hook (any size, any team count):
+    k from 16 to 4096 (every lanes-per-row layout the kernel takes, ragged
+    rows in a lane's last half-blocks), 1 to 40 groups, 1 to 700 rows, the
+    normal time limit and a zero one; every output equals the oracle's."""
+    rng = np.random.default_rng(20261203)
+    ks = [16, 48, 112, 256, 272, 592, 768, 1040, 2048, 2576, 4096]
+    for case in range(24):
+        k = int(ks[case % len(ks)])
+        groups = int(rng.integers(1, 41))
+        rows = int(rng.integers(1, 701))
+        if groups * rows * k > 12_000_000:
+            rows = max(1, 12_000_000 // (groups * k))
+        limit = 0.0 if case % 3 == 2 else 10.0
+        w = weight(1000 + case, groups, rows, k, std=float(rng.choice([0.02, 1.0, 300.0])))
+        if case % 4 == 1:
+            w[rng.integers(0, groups)] = 0
+        got = st.nvfp4_debug_quantize_weight_onepass(to_dev(w), limit_ms=limit)
+        assert_same_quant(got, oracle.quantize_weight(w),
+                          "case %d: %dx%dx%d limit %g" % (case, groups, rows, k, limit))
