@@ -252,6 +252,10 @@ def main():
     import nvfp4_token_quantization_amd as nv
     import synthgen as sg
 
+    if nv.LIB_PATH != nv.PRODUCT_LIB_PATH:
+        print("bench.py times the product library; unset NVFP4_CHECKED (the checked build "
+              "synchronizes on every call)", file=sys.stderr)
+        sys.exit(2)
     dev = torch.device("cuda:0")
     L = nv.lib()
     P = ctypes.c_void_p

@@ -42,6 +42,17 @@
  *     vectors 4-byte aligned).
  *   - Inputs must be finite; non-finite bf16 inputs give unspecified codes
  *     (no fault).  Stateless and re-entrant; calls on one stream are ordered.
+ *   - Device-side preconditions (values in device memory, which the host
+ *     never reads) are undefined when violated, never a fault: non-finite
+ *     bf16 / f32 inputs, supplied amax or scales (a supplied amax also < 0),
+ *     NaN E4M3 block-scale codes (0x7F, 0xFF) or E8M0 codes (0xFF), and
+ *     offsets that decrease.  The checked build, libnvfp4_checked.so, made
+ *     from the same sources with NVFP4_CHECKED=1, validates them on the
+ *     call's stream before launching anything else, waits for the stream
+ *     and returns NVFP4_ERROR_PRECONDITION on a violation (outputs then
+ *     untouched).  It synchronizes the host and serializes its calls, so it
+ *     is a debugging aid that cannot be captured in a graph; the product
+ *     library never checks these values and never returns that status.
  */
 #ifndef NVFP4_H
 #define NVFP4_H
@@ -58,6 +69,7 @@ extern "C" {
 #define NVFP4_ERROR_MISALIGNED 3        /* pointer alignment below the stated minimum */
 #define NVFP4_ERROR_LAUNCH 4            /* kernel launch failed */
 #define NVFP4_ERROR_ARCH 5              /* current device is not gfx950 */
+#define NVFP4_ERROR_PRECONDITION 6      /* checked build only: see below */
 
 /* Library version, major * 10000 + minor * 100 + patch. */
 int nvfp4_version(void);

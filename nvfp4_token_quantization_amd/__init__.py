@@ -29,10 +29,18 @@ import numpy as np
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libnvfp4.so")
+PRODUCT_LIB_PATH = os.path.join(_HERE, "libnvfp4.so")
+# the checked build: the same library with device-side preconditions
+# (finite inputs and scales, no NaN scale codes, non-decreasing offsets)
+# validated before every call's work; it synchronizes the host on each call
+CHECKED_LIB_PATH = os.path.join(_HERE, "libnvfp4_checked.so")
+# NVFP4_CHECKED=1 in the environment makes the binding load the checked build
+LIB_PATH = CHECKED_LIB_PATH if os.environ.get("NVFP4_CHECKED", "0") not in ("", "0") else PRODUCT_LIB_PATH
 
 SUCCESS = 0
+ERROR_PRECONDITION = 6
 _lib = None
+_loaded = {}
 
 
 class NVFP4Error(RuntimeError):
@@ -41,36 +49,46 @@ class NVFP4Error(RuntimeError):
         super().__init__("%s failed: %s (status %d)" % (fn, status_string(status), status))
 
 
+def load(path):
+    """Load one build of the library (libnvfp4.so or libnvfp4_checked.so,
+    built in-tree by ``__graft_entry__.build()``) with its C signatures."""
+    if path in _loaded:
+        return _loaded[path]
+    if not os.path.exists(path):
+        raise RuntimeError("%s is not built: run __graft_entry__.build() "
+                           "(or python -m nvfp4_token_quantization_amd.build)" % os.path.basename(path))
+    L = ctypes.CDLL(path)
+    P, I64 = ctypes.c_void_p, ctypes.c_int64
+    L.nvfp4_version.restype = ctypes.c_int
+    L.nvfp4_status_string.argtypes = [ctypes.c_int]
+    L.nvfp4_status_string.restype = ctypes.c_char_p
+    L.nvfp4_quantize_rows.argtypes = [P, I64, I64, P, P, P, P, P]
+    L.nvfp4_quantize_weight.argtypes = [P, I64, I64, I64, P, P, P, P, P, P]
+    L.nvfp4_gemm.argtypes = [P, P, P, I64, P, P, P, I64, I64, P, P]
+    L.nvfp4_grouped_gemm.argtypes = [P, P, P, I64, P, I64, P, I64, P, P, P, I64, I64, P, P]
+    L.nvfp4_grouped_gemm_swiglu.argtypes = [P, P, P, I64, P, I64, P, I64, P, P, P, I64, I64,
+                                            P, P, P]
+    L.nvfp4_swiglu_quantize_rows.argtypes = [P, I64, I64, P, P, P, P, P, P]
+    L.nvfp4_moe_route.argtypes = [P, I64, I64, I64, P, P, P, P, P]
+    L.nvfp4_dequantize_rows.argtypes = [P, P, P, I64, I64, I64, P, P]
+    L.nvfp4_mxfp8_quantize_rows.argtypes = [P, I64, I64, P, P, P]
+    L.nvfp4_mxfp8_gemm.argtypes = [P, P, I64, P, P, I64, I64, P, P]
+    L.nvfp4_mxfp8_grouped_gemm.argtypes = [P, P, I64, P, I64, P, I64, P, P, I64, I64, P, P]
+    for f in ("nvfp4_quantize_rows", "nvfp4_quantize_weight", "nvfp4_gemm",
+              "nvfp4_swiglu_quantize_rows", "nvfp4_moe_route", "nvfp4_dequantize_rows",
+              "nvfp4_mxfp8_quantize_rows", "nvfp4_mxfp8_gemm", "nvfp4_mxfp8_grouped_gemm",
+              "nvfp4_grouped_gemm", "nvfp4_grouped_gemm_swiglu"):
+        getattr(L, f).restype = ctypes.c_int
+    _loaded[path] = L
+    return L
+
+
 def lib():
-    """Load libnvfp4.so (built in-tree by ``__graft_entry__.build()``)."""
+    """The library every call goes through: LIB_PATH (the product build
+    unless NVFP4_CHECKED is set)."""
     global _lib
     if _lib is None:
-        if not os.path.exists(LIB_PATH):
-            raise RuntimeError("libnvfp4.so is not built: run __graft_entry__.build() "
-                               "(or python -m nvfp4_token_quantization_amd.build)")
-        L = ctypes.CDLL(LIB_PATH)
-        P, I64 = ctypes.c_void_p, ctypes.c_int64
-        L.nvfp4_version.restype = ctypes.c_int
-        L.nvfp4_status_string.argtypes = [ctypes.c_int]
-        L.nvfp4_status_string.restype = ctypes.c_char_p
-        L.nvfp4_quantize_rows.argtypes = [P, I64, I64, P, P, P, P, P]
-        L.nvfp4_quantize_weight.argtypes = [P, I64, I64, I64, P, P, P, P, P, P]
-        L.nvfp4_gemm.argtypes = [P, P, P, I64, P, P, P, I64, I64, P, P]
-        L.nvfp4_grouped_gemm.argtypes = [P, P, P, I64, P, I64, P, I64, P, P, P, I64, I64, P, P]
-        L.nvfp4_grouped_gemm_swiglu.argtypes = [P, P, P, I64, P, I64, P, I64, P, P, P, I64, I64,
-                                                P, P, P]
-        L.nvfp4_swiglu_quantize_rows.argtypes = [P, I64, I64, P, P, P, P, P, P]
-        L.nvfp4_moe_route.argtypes = [P, I64, I64, I64, P, P, P, P, P]
-        L.nvfp4_dequantize_rows.argtypes = [P, P, P, I64, I64, I64, P, P]
-        L.nvfp4_mxfp8_quantize_rows.argtypes = [P, I64, I64, P, P, P]
-        L.nvfp4_mxfp8_gemm.argtypes = [P, P, I64, P, P, I64, I64, P, P]
-        L.nvfp4_mxfp8_grouped_gemm.argtypes = [P, P, I64, P, I64, P, I64, P, P, I64, I64, P, P]
-        for f in ("nvfp4_quantize_rows", "nvfp4_quantize_weight", "nvfp4_gemm",
-                  "nvfp4_swiglu_quantize_rows", "nvfp4_moe_route", "nvfp4_dequantize_rows",
-                  "nvfp4_mxfp8_quantize_rows", "nvfp4_mxfp8_gemm", "nvfp4_mxfp8_grouped_gemm",
-                  "nvfp4_grouped_gemm", "nvfp4_grouped_gemm_swiglu"):
-            getattr(L, f).restype = ctypes.c_int
-        _lib = L
+        _lib = load(LIB_PATH)
     return _lib
 
 

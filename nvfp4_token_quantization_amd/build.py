@@ -1,6 +1,9 @@
-"""Build libnvfp4.so (HIP, gfx950) and the test-only codec self-test library
-libnvfp4_selftest.so in-tree with hipcc: one object per source, compiled in
-parallel, then linked into the shared libraries."""
+"""Build libnvfp4.so (HIP, gfx950), its checked variant libnvfp4_checked.so
+(the same sources with NVFP4_CHECKED=1 plus checks.hip: device-side
+preconditions validated before each call's work) and the test-only codec
+self-test library libnvfp4_selftest.so in-tree with hipcc: one object per
+source and flag set, compiled in parallel, then linked into the shared
+libraries."""
 import os
 import subprocess
 import sys
@@ -12,6 +15,9 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libnvfp4.so")
 SOURCES = ["abi_common.hip", "host_util.hip", "quantize.hip", "swiglu_quantize.hip", "route.hip",
            "dequantize.hip", "mxfp8.hip", "mxfp8_gemm.hip", "gemm.hip", "gemm_skinny.hip"]
+CHECKED_LIB = os.path.join(HERE, "libnvfp4_checked.so")
+CHECKED_SOURCES = SOURCES + ["checks.hip"]
+CHECKED_FLAGS = ("-DNVFP4_CHECKED=1",)
 SELFTEST_LIB = os.path.join(HERE, "libnvfp4_selftest.so")
 SELFTEST_SOURCES = ["selftest.hip", "host_util.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -39,39 +45,43 @@ def _run(cmd):
 
 
 def build(verbose=False, sources=None, lib=None, jobs=None, extra_flags=()):
-    """Compile and link the libraries.  By default: libnvfp4.so from SOURCES
-    and libnvfp4_selftest.so from SELFTEST_SOURCES (each source compiled
-    once).  With `sources` and `lib`: that one library.  `extra_flags` are
-    added to every compile.  Returns the path of the (first) library."""
+    """Compile and link the libraries.  By default: libnvfp4.so from SOURCES,
+    libnvfp4_checked.so from CHECKED_SOURCES with CHECKED_FLAGS and
+    libnvfp4_selftest.so from SELFTEST_SOURCES.  With `sources` and `lib`:
+    that one library.  `extra_flags` are added to every compile.  Returns the
+    path of the (first) library."""
     if sources or lib:
-        targets = [(lib or LIB, list(sources or SOURCES))]
+        targets = [(lib or LIB, list(sources or SOURCES), ())]
     else:
-        targets = [(LIB, SOURCES), (SELFTEST_LIB, SELFTEST_SOURCES)]
-    allsrc = sorted({s for _, srcs in targets for s in srcs})
+        targets = [(LIB, SOURCES, ()), (CHECKED_LIB, CHECKED_SOURCES, CHECKED_FLAGS),
+                   (SELFTEST_LIB, SELFTEST_SOURCES, ())]
+    units = sorted({(s, fl) for _, srcs, fl in targets for s in srcs})
     objdir = os.path.join(os.path.dirname(os.path.abspath(targets[0][0])), "_build")
     os.makedirs(objdir, exist_ok=True)
     inc = ["-I", os.path.join(ROOT, "include"), "-I", CSRC]
     tag = "%d" % os.getpid()
-    jobs = jobs or min(len(allsrc), int(os.environ.get("MAX_JOBS", "8")), os.cpu_count() or 1)
+    jobs = jobs or min(len(units), int(os.environ.get("MAX_JOBS", "8")), os.cpu_count() or 1)
 
-    def compile_one(src):
-        obj = os.path.join(objdir, os.path.splitext(src)[0] + "." + tag + ".o")
-        cmd = [HIPCC] + FLAGS + list(extra_flags) + inc + ["-c", os.path.join(CSRC, src), "-o", obj]
+    def compile_one(unit):
+        src, fl = unit
+        kind = "checked." if fl else ""
+        obj = os.path.join(objdir, os.path.splitext(src)[0] + "." + kind + tag + ".o")
+        cmd = [HIPCC] + FLAGS + list(fl) + list(extra_flags) + inc + ["-c", os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         rc, msg = _run(cmd)
-        return src, obj, rc, msg
+        return unit, obj, rc, msg
 
     with ThreadPoolExecutor(max_workers=jobs) as ex:
-        results = list(ex.map(compile_one, allsrc))
-    obj_of = {s: o for s, o, _, _ in results}
-    failed = [(s, m) for s, _, rc, m in results if rc != 0]
+        results = list(ex.map(compile_one, units))
+    obj_of = {u: o for u, o, _, _ in results}
+    failed = [(u[0], m) for u, _, rc, m in results if rc != 0]
     try:
         if failed:
             raise RuntimeError("hipcc failed:\n" + "\n".join("%s:\n%s" % f for f in failed))
-        for path, srcs in targets:
+        for path, srcs, fl in targets:
             tmp = path + ".tmp" + tag
-            cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC"] + [obj_of[s] for s in srcs]
+            cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC"] + [obj_of[(s, fl)] for s in srcs]
             cmd += ["-o", tmp]
             if verbose:
                 print(" ".join(cmd), flush=True)

@@ -13,6 +13,8 @@ const char* nvfp4_status_string(int status) {
     case NVFP4_ERROR_MISALIGNED: return "misaligned pointer";
     case NVFP4_ERROR_LAUNCH: return "kernel launch failed";
     case NVFP4_ERROR_ARCH: return "current device is not gfx950";
+    case NVFP4_ERROR_PRECONDITION:
+      return "device-side precondition violated (non-finite input or scale, NaN scale code, decreasing offsets)";
     default: return "unknown status";
   }
 }

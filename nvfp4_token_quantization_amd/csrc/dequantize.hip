@@ -169,6 +169,14 @@ extern "C" int nvfp4_dequantize_rows(const uint8_t* q, const uint8_t* sb, const 
   if (!aligned(q, 16) || !aligned(s, 4) || !aligned(x_bf16, 16)) return NVFP4_ERROR_MISALIGNED;
   int st = nvfp4host::check_arch();
   if (st) return st;
+#if NVFP4_CHECKED
+  {
+    nvfp4check::Checks chk((hipStream_t)stream);
+    chk.e4m3_codes(sb, rows * (k / 16));
+    chk.f32_finite(s, (rows + rows_per_scale - 1) / rows_per_scale);
+    if ((st = chk.result())) return st;
+  }
+#endif
   const int nh = (int)(k / 8);  // 8-element half-blocks per row
   int lanes = 64;
   nvfp4::DeqKernel kern = nvfp4::pick_dequant_kernel(nh, lanes);

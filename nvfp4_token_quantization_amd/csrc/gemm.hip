@@ -839,6 +839,16 @@ extern "C" int nvfp4_gemm(const uint8_t* a_q, const uint8_t* a_sb, const float* 
     return NVFP4_ERROR_MISALIGNED;
   int st = nvfp4host::check_arch();
   if (st) return st;
+#if NVFP4_CHECKED
+  {
+    nvfp4check::Checks chk((hipStream_t)stream);
+    chk.e4m3_codes(a_sb, m * (k / 16));
+    chk.f32_finite(a_s, m);
+    chk.e4m3_codes(b_sb, n * (k / 16));
+    chk.f32_finite(b_s, 1);
+    if ((st = chk.result())) return st;
+  }
+#endif
   hipStream_t str = (hipStream_t)stream;
   if (k == 0) {
     hipLaunchKernelGGL(nvfp4::zero_rows_kernel, dim3(1024), dim3(256), 0, str, y, m * n);
@@ -873,6 +883,17 @@ extern "C" int nvfp4_grouped_gemm(const uint8_t* a_q, const uint8_t* a_sb, const
     return NVFP4_ERROR_MISALIGNED;
   int st = nvfp4host::check_arch();
   if (st) return st;
+#if NVFP4_CHECKED
+  {
+    nvfp4check::Checks chk((hipStream_t)stream);
+    chk.e4m3_codes(a_sb, a_rows * (k / 16));
+    chk.f32_finite(a_s, a_rows);
+    chk.e4m3_codes(b_sb, groups * n * (k / 16));
+    chk.f32_finite(b_s, groups);
+    chk.offsets(offsets, groups);
+    if ((st = chk.result())) return st;
+  }
+#endif
   hipStream_t str = (hipStream_t)stream;
   nvfp4::GemmArgs p{};
   p.a_q = a_q; p.a_sb = a_sb; p.a_s = a_s; p.a_rows = a_rows;
@@ -905,6 +926,17 @@ extern "C" int nvfp4_grouped_gemm_swiglu(const uint8_t* a_q, const uint8_t* a_sb
     return NVFP4_ERROR_MISALIGNED;
   int st = nvfp4host::check_arch();
   if (st) return st;
+#if NVFP4_CHECKED
+  {
+    nvfp4check::Checks chk((hipStream_t)stream);
+    chk.e4m3_codes(a_sb, a_rows * (k / 16));
+    chk.f32_finite(a_s, a_rows);
+    chk.e4m3_codes(b_sb, groups * 2 * f * (k / 16));
+    chk.f32_finite(b_s, groups);
+    chk.offsets(offsets, groups);
+    if ((st = chk.result())) return st;
+  }
+#endif
   hipStream_t str = (hipStream_t)stream;
   // the row maxima are atomic maxima over the column tiles: start from zero
   // (a fill kernel, so the sequence can be captured in a graph)

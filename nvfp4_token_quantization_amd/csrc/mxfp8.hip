@@ -71,6 +71,13 @@ extern "C" int nvfp4_mxfp8_quantize_rows(const uint16_t* x_bf16, int64_t rows, i
   if (!aligned(x_bf16, 16) || !aligned(q, 16)) return NVFP4_ERROR_MISALIGNED;
   int st = nvfp4host::check_arch();
   if (st) return st;
+#if NVFP4_CHECKED
+  {
+    nvfp4check::Checks chk((hipStream_t)stream);
+    chk.bf16_finite(x_bf16, rows * k);
+    if ((st = chk.result())) return st;
+  }
+#endif
   const int64_t nchunks = rows * (k / 8);  // 16-byte chunks, 4 per block
   constexpr int U = 4;
   const int64_t need = (nchunks + 256 * U - 1) / (256 * U);

@@ -257,6 +257,16 @@ extern "C" int nvfp4_mxfp8_gemm(const uint8_t* a_q, const uint8_t* a_sc, int64_t
   if (!aligned(a_q, 16) || !aligned(b_q, 16) || !aligned(y, 16)) return NVFP4_ERROR_MISALIGNED;
   int st = nvfp4host::check_arch();
   if (st) return st;
+#if NVFP4_CHECKED
+  {
+    nvfp4check::Checks chk((hipStream_t)stream);
+    chk.e4m3_codes(a_q, m * k);
+    chk.e8m0_codes(a_sc, m * (k / 32));
+    chk.e4m3_codes(b_q, n * k);
+    chk.e8m0_codes(b_sc, n * (k / 32));
+    if ((st = chk.result())) return st;
+  }
+#endif
   nvfp4::MxGemmArgs p{};
   p.a_q = a_q; p.a_sc = a_sc; p.a_rows = m; p.row_index = nullptr;
   p.b_q = b_q; p.b_sc = b_sc; p.n = n; p.k = k; p.y = y;
@@ -285,6 +295,17 @@ extern "C" int nvfp4_mxfp8_grouped_gemm(const uint8_t* a_q, const uint8_t* a_sc,
     return NVFP4_ERROR_MISALIGNED;
   int st = nvfp4host::check_arch();
   if (st) return st;
+#if NVFP4_CHECKED
+  {
+    nvfp4check::Checks chk((hipStream_t)stream);
+    chk.e4m3_codes(a_q, a_rows * k);
+    chk.e8m0_codes(a_sc, a_rows * (k / 32));
+    chk.e4m3_codes(b_q, groups * n * k);
+    chk.e8m0_codes(b_sc, groups * n * (k / 32));
+    chk.offsets(offsets, groups);
+    if ((st = chk.result())) return st;
+  }
+#endif
   nvfp4::MxGemmArgs p{};
   p.a_q = a_q; p.a_sc = a_sc; p.a_rows = a_rows; p.row_index = row_index;
   p.b_q = b_q; p.b_sc = b_sc; p.n = n; p.k = k; p.y = y;

@@ -220,3 +220,29 @@ int64_t wall_clock_khz();
 int launch_status();
 
 }  // namespace nvfp4host
+
+#if NVFP4_CHECKED
+// Device-side precondition checks of the checked build (checks.hip).  The
+// constructor takes a library-wide lock and clears the violation flag on
+// `stream`; each method launches one validation kernel there; result()
+// waits for the stream and returns NVFP4_SUCCESS, NVFP4_ERROR_PRECONDITION
+// or NVFP4_ERROR_LAUNCH, and releases the lock.  Null pointers and empty
+// ranges check nothing.
+namespace nvfp4check {
+
+struct Checks {
+  explicit Checks(hipStream_t s);
+  ~Checks();
+  void bf16_finite(const uint16_t* x, int64_t n);
+  void f32_finite(const float* x, int64_t n, bool nonneg = false);
+  void e4m3_codes(const uint8_t* c, int64_t n);  // no NaN code (0x7F, 0xFF)
+  void e8m0_codes(const uint8_t* c, int64_t n);  // no NaN code (0xFF)
+  void offsets(const int32_t* off, int64_t groups);  // off[0..groups] non-decreasing
+  int result();
+
+  hipStream_t stream;
+  bool done = false;
+};
+
+}  // namespace nvfp4check
+#endif

@@ -252,6 +252,14 @@ extern "C" int nvfp4_quantize_rows(const uint16_t* x_bf16, int64_t rows, int64_t
     return NVFP4_ERROR_MISALIGNED;
   int st = nvfp4host::check_arch();
   if (st) return st;
+#if NVFP4_CHECKED
+  {
+    nvfp4check::Checks chk((hipStream_t)stream);
+    chk.bf16_finite(x_bf16, rows * k);
+    chk.f32_finite(amax_in, rows, true);
+    if ((st = chk.result())) return st;
+  }
+#endif
   hipStream_t str = (hipStream_t)stream;
   if (k == 0) {
     dim3 grid((unsigned)((rows + 255) / 256));
@@ -287,6 +295,14 @@ extern "C" int nvfp4_quantize_weight(const uint16_t* w_bf16, int64_t groups, int
   if (amax_out && amax_out < s + groups && s < amax_out + groups) return NVFP4_ERROR_INVALID_VALUE;
   int st = nvfp4host::check_arch();
   if (st) return st;
+#if NVFP4_CHECKED
+  {
+    nvfp4check::Checks chk((hipStream_t)stream);
+    chk.bf16_finite(w_bf16, rows * k);
+    chk.f32_finite(amax_in, groups, true);
+    if ((st = chk.result())) return st;
+  }
+#endif
   hipStream_t str = (hipStream_t)stream;
   // one HBM pass when each group is large enough and a team of workgroups
   // holds it in registers (weight_onepass.h)

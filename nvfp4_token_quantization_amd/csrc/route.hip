@@ -209,6 +209,13 @@ extern "C" int nvfp4_moe_route(const float* logits, int64_t tokens, int64_t num_
     return NVFP4_ERROR_MISALIGNED;
   int st = nvfp4host::check_arch();
   if (st) return st;
+#if NVFP4_CHECKED
+  {
+    nvfp4check::Checks chk((hipStream_t)stream);
+    chk.f32_finite(logits, tokens * num_experts);
+    if ((st = chk.result())) return st;
+  }
+#endif
   hipStream_t str = (hipStream_t)stream;
   const int E = (int)num_experts, K = (int)topk;
   if (tokens > 0) {

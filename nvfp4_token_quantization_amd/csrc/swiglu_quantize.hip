@@ -213,6 +213,13 @@ extern "C" int nvfp4_swiglu_quantize_rows(const float* gate_up, int64_t rows, in
     return NVFP4_ERROR_MISALIGNED;
   int st = nvfp4host::check_arch();
   if (st) return st;
+#if NVFP4_CHECKED
+  {
+    nvfp4check::Checks chk((hipStream_t)stream);
+    chk.f32_finite(gate_up, rows * 2 * f);
+    if ((st = chk.result())) return st;
+  }
+#endif
   int wpr = 1;
   nvfp4::SwigluKernel kern = nvfp4::pick_swiglu(f, wpr);
   if (!kern) return NVFP4_ERROR_UNSUPPORTED_SHAPE;

@@ -1,11 +1,13 @@
 """Host-side checks of the C ABI (no GPU needed).
 
-- libnvfp4.so loads and exports every function include/nvfp4.h declares and
-  no self-test hook; libnvfp4_selftest.so exports those include/
-  nvfp4_selftest.h declares;
-- argument errors return the documented status before any HIP call
-  (null pointers, negative sizes, k % 16 != 0, misaligned pointers, zero
-  groups), and empty problems return success without launching.
+- libnvfp4.so and its checked build libnvfp4_checked.so load and export
+  every function include/nvfp4.h declares and no self-test hook;
+  libnvfp4_selftest.so exports those include/nvfp4_selftest.h declares; the
+  device-side precondition checks exist only in the checked build;
+- in both builds, argument errors return the documented status before any
+  HIP call (null pointers, negative sizes, k % 16 != 0, misaligned
+  pointers, zero groups), and empty problems return success without
+  launching.
 """
 import ctypes
 import os
@@ -20,10 +22,10 @@ SELFTEST_HEADER = os.path.join(ROOT, "include", "nvfp4_selftest.h")
 OK, INVALID, SHAPE, MISALIGNED = 0, 1, 2, 3
 
 
-@pytest.fixture(scope="module")
-def L():
+@pytest.fixture(scope="module", params=["product", "checked"])
+def L(request):
     import nvfp4_token_quantization_amd as nv
-    return nv.lib()
+    return nv.load(nv.PRODUCT_LIB_PATH if request.param == "product" else nv.CHECKED_LIB_PATH)
 
 
 @pytest.fixture(scope="module")
@@ -61,11 +63,19 @@ def test_selftest_hooks_live_outside_the_product_library(L, S):
 
 
 def test_status_strings_and_version(L):
+    assert L.nvfp4_version() == 100
+    for st in range(7):
+        assert L.nvfp4_status_string(st) != b"unknown status"
+    assert b"precondition" in L.nvfp4_status_string(6)
+    assert L.nvfp4_status_string(99) == b"unknown status"
+
+
+def test_precondition_checks_only_in_the_checked_build():
     import nvfp4_token_quantization_amd as nv
-    assert nv.version() == 100
-    for st in range(6):
-        assert nv.status_string(st)
-    assert nv.status_string(99) == "unknown status"
+    check_symbol = "_ZN10nvfp4check6Checks6resultEv"  # nvfp4check::Checks::result()
+    assert hasattr(nv.load(nv.CHECKED_LIB_PATH), check_symbol)
+    assert not hasattr(nv.load(nv.PRODUCT_LIB_PATH), check_symbol)
+    assert nv.LIB_PATH == nv.PRODUCT_LIB_PATH or os.environ.get("NVFP4_CHECKED")
 
 
 FAKE = 0x10000          # 16-byte aligned, never dereferenced (errors return first)
