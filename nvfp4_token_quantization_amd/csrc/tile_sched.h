@@ -37,9 +37,24 @@ struct TileRange {
 // clamped row range [s_lo[e], s_hi[e]).  Offsets are clamped to [0, m_total]
 // and made non-decreasing, so bad metadata cannot address rows outside the
 // output.  Four 64-expert segments per round of coalesced loads (lane l reads
-// offsets e and e + 1 of expert e = 64 i + l), a wave scan per segment; all
-// arithmetic in 32 bits (offsets are int32).  The caller synchronizes before
-// reading the arrays.
+// offsets e and e + 1 of expert e = 64 i + l), a wave scan per segment
+// (segments past G are skipped); all arithmetic in 32 bits (offsets are
+// int32).  The caller synchronizes before reading the arrays.
+// Inclusive prefix sum over the 64 lanes of a wave in DPP moves (no LDS
+// permutes): shifts right by 1, 2, 4 and 8 lanes inside each 16-lane row
+// (lanes shifted in from outside the row read 0), then lane 15's sum added to
+// rows 1 and 3 (row_bcast:15, row mask 0b1010) and lane 31's to rows 2 and 3
+// (row_bcast:31, row mask 0b1100); rows outside a mask add 0.
+__device__ __forceinline__ int32_t wave_incl_scan(int32_t v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, false);  // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, false);  // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, false);  // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, false);  // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false);  // row_bcast:15
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false);  // row_bcast:31
+  return v;
+}
+
 template <int BM>
 __device__ __forceinline__ void expert_tile_prefix(const int32_t* offsets, int G, int64_t m_total,
                                                    int lane, int32_t* s_prefix, int32_t* s_lo,
@@ -51,27 +66,25 @@ __device__ __forceinline__ void expert_tile_prefix(const int32_t* offsets, int G
 #pragma unroll
     for (int i = 0; i < 4; ++i) {  // every load first, so they are in flight together
       const int e = e0 + 64 * i + lane;
-      o0[i] = offsets[min(e, G)];
-      o1[i] = offsets[min(e + 1, G)];
+      if (e0 + 64 * i < G) {
+        o0[i] = offsets[min(e, G)];
+        o1[i] = offsets[min(e + 1, G)];
+      }
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
+      if (e0 + 64 * i >= G) break;
       const int e = e0 + 64 * i + lane;
       const int32_t lo = min(max(o0[i], 0), mt);
       const int32_t hi = min(max(o1[i], lo), mt);
       const int32_t c = e < G ? (int32_t)(((uint32_t)(hi - lo) + (BM - 1)) / BM) : 0;
-      int32_t incl = c;
-#pragma unroll
-      for (int d = 1; d < 64; d <<= 1) {
-        const int32_t o = __shfl_up(incl, d, 64);
-        if (lane >= d) incl += o;
-      }
+      const int32_t incl = wave_incl_scan(c);
       if (e < G) {
         s_prefix[e] = carry + incl - c;
         s_lo[e] = lo;
         s_hi[e] = hi;
       }
-      carry += __shfl(incl, 63, 64);
+      carry += __builtin_amdgcn_readlane(incl, 63);
     }
   }
   if (lane == 0) s_prefix[G] = carry;
@@ -86,10 +99,11 @@ __device__ __forceinline__ int find_expert(const int32_t* s_prefix, int G, int m
   for (int e0 = 0; e0 < G; e0 += 256) {
     int32_t v[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) v[i] = s_prefix[min(e0 + 64 * i + lane, G)];
+    for (int i = 0; i < 4; ++i)
+      if (e0 + 64 * i < G) v[i] = s_prefix[min(e0 + 64 * i + lane, G)];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      count += __popcll(__ballot(e0 + 64 * i + lane < G && v[i] <= mt));
+      if (e0 + 64 * i < G) count += __popcll(__ballot(e0 + 64 * i + lane < G && v[i] <= mt));
   }
   return count - 1;
 }
@@ -114,7 +128,8 @@ __device__ __forceinline__ int64_t gathered_row(const int32_t* row_index, int64_
 // each XCD owns one region of an (8 / xcd_n) x xcd_n split of the tile grid
 // so its L2 holds that region's A rows and B columns.  Inside a region, n runs
 // fastest.  Grouped: every block derives the per-expert m-tile prefix from the
-// device offsets (a wave scan into s_prefix) and binary-searches its expert.
+// device offsets (a wave scan, in registers for up to 256 experts, else into
+// s_prefix) and finds its expert by a ballot count.
 // Returns false when the block has no tile (block-uniform).  Called by the
 // whole block (one wave of 64 lanes).
 template <int BM, int BN>
@@ -152,7 +167,56 @@ __device__ __forceinline__ bool schedule_tile(const TileGrid& t, int lane,
   int jf = 0, hf = -1, mt, nt;
   int64_t row_lo, row_hi;
   int g = 0;
-  if (t.offsets) {
+  if (t.offsets && t.groups <= 256) {
+    // Up to 256 experts: one round of offset loads, and the m-tile prefix,
+    // the expert lookup and its row range stay in registers (no LDS round
+    // trip, no barrier).  Same arithmetic as expert_tile_prefix and
+    // find_expert: lo / hi the clamped row range of expert 64 i + lane, ex
+    // the m-tiles of the experts before it; the expert's values come from its
+    // lane by readlane.
+    const int G = t.groups;
+    const int32_t mtot = (int32_t)min(t.m_total, (int64_t)0x7FFFFFFF);
+    int32_t o0[4], o1[4], lo[4] = {0, 0, 0, 0}, hi[4] = {0, 0, 0, 0}, ex[4] = {0, 0, 0, 0};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = 64 * i + lane;
+      if (64 * i < G) {
+        o0[i] = t.offsets[min(e, G)];
+        o1[i] = t.offsets[min(e + 1, G)];
+      }
+    }
+    int32_t carry = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (64 * i >= G) break;
+      const int e = 64 * i + lane;
+      lo[i] = min(max(o0[i], 0), mtot);
+      hi[i] = min(max(o1[i], lo[i]), mtot);
+      const int32_t c = e < G ? (int32_t)(((uint32_t)(hi[i] - lo[i]) + (BM - 1)) / BM) : 0;
+      const int32_t incl = wave_incl_scan(c);
+      ex[i] = carry + incl - c;
+      carry += __builtin_amdgcn_readlane(incl, 63);
+    }
+    const int total_mt = carry;
+    const int mpx = (total_mt + XM - 1) / XM;
+    const int mcount = min(mpx, max(total_mt - xm * mpx, 0));
+    if (!place(mcount, jf, hf)) return false;  // block-uniform
+    mt = xm * mpx + jf / width;
+    nt = nlo + jf % width;
+    int count = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (64 * i < G) count += __popcll(__ballot(64 * i + lane < G && ex[i] <= mt));
+    g = max(count - 1, 0);
+    const int seg = g >> 6, ln = g & 63;
+    int32_t lo_s = lo[0], hi_s = hi[0], ex_s = ex[0];
+#pragma unroll
+    for (int i = 1; i < 4; ++i)
+      if (seg == i) { lo_s = lo[i]; hi_s = hi[i]; ex_s = ex[i]; }
+    row_lo = (int64_t)__builtin_amdgcn_readlane(lo_s, ln) +
+             (int64_t)(mt - __builtin_amdgcn_readlane(ex_s, ln)) * BM;
+    row_hi = min((int64_t)__builtin_amdgcn_readlane(hi_s, ln), row_lo + BM);
+  } else if (t.offsets) {
     const int G = t.groups;
     int32_t* s_lo = s_prefix + (MAX_GROUPS + 1);
     int32_t* s_hi = s_prefix + 2 * (MAX_GROUPS + 1);
