@@ -2,6 +2,9 @@
 
 - the largest expert count the ABI accepts (1024 groups), NVFP4 and MXFP8:
   the per-expert tile prefix then needs its entry 1024 (the total);
+- expert counts on both sides of the schedule's 64-expert scan segments and
+  of its 256-expert switch from registers to LDS (1 to 513 experts), in
+  the few-rows and the tiled kernels;
 - an output whose address has bit 31 of its low 32-bit word set, through
   every branch of the LDS kernel's epilogue (n % 4 == 0 through LDS, whole
   tiles, per element): the epilogue's buffer resource takes the tile's base
@@ -80,6 +83,51 @@ def test_grouped_1024_groups_tiled_kernel():
     check_gemm(y, y_ref, bound, "1024 groups, tiled, %d rows" % m_total)
 
 
+def _counts_any(seed, groups, scale):
+    # empty, tiny and a few larger experts; the last expert non-empty, the
+    # middle one over one 128-row tile (one expert: 9 or 72 rows)
+    if groups == 1:
+        return np.array([9 * scale], np.int64)
+    u = sg.uniform(seed, 1, groups)
+    counts = np.where(u < 0.5, 0, np.where(u < 0.9, 1 + (u * 97).astype(np.int64) % 4,
+                                             (u * 1000).astype(np.int64) % 80))
+    counts = counts * scale
+    counts[-1] = 37
+    counts[groups // 2] = 129
+    return counts.astype(np.int64)
+
+
+@pytest.mark.parametrize("groups", [1, 63, 64, 65, 255, 256, 257, 300, 513])
+@pytest.mark.parametrize("scale", [1, 8])
+def test_grouped_expert_counts_across_scan_segments(groups, scale):
+    """scale 1: few rows per expert (the few-rows kernel, whose workgroups scan
+    the offsets into LDS); scale 8: more than 16 rows per expert on average
+    (the tiled kernel: the expert prefix in registers up to 256 experts, in
+    LDS above).  Segment boundaries at 64, 256 and the partial last segment
+    of the second round at 300 and 513."""
+    counts = _counts_any(520 + groups, groups, scale)
+    n, k, tokens = 64, 256, 211
+    if scale > 1:
+        assert counts.sum() > 16 * groups
+    else:
+        assert counts.sum() <= 16 * groups
+    x = sg.student_t3_bf16(521, 1, (tokens, k))
+    a = oracle.quantize_rows(x)
+    w = sg.normal_bf16(522 + groups, 2, (groups, n, k), 0.0, 0.02)
+    b = oracle.quantize_weight(w)[:3]
+    offsets = np.zeros(groups + 1, np.int32)
+    offsets[1:] = np.cumsum(counts)
+    m_total = int(offsets[-1])
+    ri = ((np.arange(m_total) * 7919) % tokens).astype(np.int32)
+    y = torch.full((m_total + 3, n), float("nan"), device=dev())
+    nv.nvfp4_grouped_gemm(dev_op(a), to_dev(offsets), dev_op(b), row_index=to_dev(ri),
+                          m_total=m_total, out=y)
+    y = to_np(y)
+    y_ref, bound = oracle.grouped_gemm(a, offsets, b, row_index=ri)
+    check_gemm(y[:m_total], y_ref, bound, "%d groups x%d, %d rows" % (groups, scale, m_total))
+    assert np.all(np.isnan(y[m_total:])), "rows past offsets[groups] must not be written"
+
+
 def test_mxfp8_grouped_1024_groups():
     from test_gpu_mxfp8 import check_mx_gemm, grouped_reference
     counts = _counts_1024(511)
@@ -98,6 +146,24 @@ def test_mxfp8_grouped_1024_groups():
     y_ref, bound = grouped_reference(aq, asc, {"offsets": offsets, "row_index": ri}, wq, wsc)
     check_mx_gemm(y[:m_total], y_ref, bound, "MXFP8, 1024 groups")
     assert np.all(np.isnan(y[m_total:]))
+
+
+@pytest.mark.parametrize("groups", [65, 257, 300])
+def test_mxfp8_grouped_expert_counts_across_scan_segments(groups):
+    from test_gpu_mxfp8 import check_mx_gemm, grouped_reference
+    counts = _counts_any(530 + groups, groups, 8)
+    n, k, tokens = 64, 128, 199
+    aq, asc = oracle.mxfp8_quantize_rows(sg.student_t3_bf16(531, sg.S_X, (tokens, k)))
+    wq, wsc = oracle.mxfp8_quantize_rows(sg.normal_bf16(532 + groups, sg.S_W, (groups * n, k), 0.0, 0.02))
+    wq, wsc = wq.reshape(groups, n, k), wsc.reshape(groups, n, k // 32)
+    offsets = np.zeros(groups + 1, np.int32)
+    offsets[1:] = np.cumsum(counts)
+    m_total = int(offsets[-1])
+    ri = ((np.arange(m_total) * 7919) % tokens).astype(np.int32)
+    y = to_np(nv.nvfp4_mxfp8_grouped_gemm((to_dev(aq), to_dev(asc)), to_dev(offsets),
+                                          (to_dev(wq), to_dev(wsc)), row_index=to_dev(ri)))
+    y_ref, bound = grouped_reference(aq, asc, {"offsets": offsets, "row_index": ri}, wq, wsc)
+    check_mx_gemm(y, y_ref, bound, "MXFP8, %d groups" % groups)
 
 
 # -------------------------------------------- output address, bit 31 set --
