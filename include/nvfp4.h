@@ -299,6 +299,12 @@ int nvfp4_mxfp8_grouped_gemm(const uint8_t* a_q, const uint8_t* a_sc, int64_t a_
  * that the guarantee is the (k/16 + 2) 2^-24 bound (6.1e-5 at k = 16384).
  * Tests at k = 8192 and 16384 with same-sign operands, where rounding errors
  * cannot cancel, observe at most 2e-6 sum_k |a_k b_k|.
+ * Determinism: repeated calls give identical bits, and each output row
+ * depends only on its own A row and B once the kernel is chosen.  m <= 64
+ * with k % 256 == 0 takes the few-rows kernel, whose K-split partial sums
+ * round differently from the tiled kernels taken otherwise.  So a row's last
+ * bits can differ between a call with m <= 64 and one with m > 64, both
+ * within the bound above.
  * Errors: INVALID_VALUE, UNSUPPORTED_SHAPE (k % 16 != 0), MISALIGNED, ARCH,
  * LAUNCH.  m, n or k == 0 are allowed (k == 0 writes zeros).
  */
@@ -325,7 +331,10 @@ int nvfp4_gemm(const uint8_t* a_q, const uint8_t* a_sb, const float* a_s, int64_
  *             [0, m_total]; rows at or past offsets[groups] are not written.
  *   B: b_q [groups, n, k/2], b_sb [groups, n, k/16], b_s [groups] (per expert)
  *   y  [m_total, n] f32 out
- * Accuracy as nvfp4_gemm.  groups <= 1024.
+ * Accuracy as nvfp4_gemm.  groups <= 1024.  Determinism as nvfp4_gemm.  The
+ * kernel choice follows the whole layout: at most 16 routed rows per expert
+ * on average (m_total <= 16 groups) with k % 256 == 0 takes the few-rows
+ * kernel.
  * Errors: INVALID_VALUE (groups < 1, negative sizes, null pointers),
  * UNSUPPORTED_SHAPE (k % 16 != 0, groups > 1024), MISALIGNED, ARCH, LAUNCH.
  */

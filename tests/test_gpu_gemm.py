@@ -133,6 +133,22 @@ def test_dense_deterministic():
         assert torch.equal(nv.nvfp4_gemm(ad, bd), y0)
 
 
+@pytest.mark.parametrize("k", [2048, 640])
+def test_dense_rows_batch_invariant_tiled(k):
+    """The tiled kernels (m > 64; k = 2048 takes the LDS-staged kernel, 640
+    the register-direct one) compute each output row from its own A row in
+    a fixed order: rows 70..199 of a 300-row call equal a 130-row call on
+    those rows, bit for bit, though they sit at other tile positions (and
+    the 130-row call's last round is issued as half tiles)."""
+    a, b = quant_pair(19, 300, 333, k)
+    bd = (to_dev(b[0][0]), to_dev(b[1][0]), to_dev(b[2]))
+    ad = dev_op(a)
+    y = nv.nvfp4_gemm(ad, bd)
+    sub = tuple(t[70:200].contiguous() for t in ad)
+    ys = nv.nvfp4_gemm(sub, bd)
+    assert torch.equal(ys, y[70:200])
+
+
 # ---------------------------------------------------------------- grouped --
 def grouped_case(seed, tokens, counts, n, k, row_index=True):
     groups = len(counts)
