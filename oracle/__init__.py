@@ -355,6 +355,18 @@ def grouped_gemm(a, offsets, b, row_index=None, m_total=None):
     if m_total is None:
         m_total = int(off[-1])
     ri = None if row_index is None else _c(row_index, np.int32)
+    # preconditions of this reference (the library's handling of bad
+    # metadata, clamped offsets and zero rows for indices outside A, is
+    # checked against expected values built separately): non-decreasing
+    # offsets within the output, and every row read inside A
+    if off.size != groups + 1 or off[0] < 0 or np.any(np.diff(off) < 0) or off[-1] > m_total:
+        raise ValueError("offsets must be non-decreasing, start at >= 0 and end at <= m_total")
+    used = int(off[-1])
+    if ri is None:
+        if used > aq.shape[0]:
+            raise ValueError("without row_index, A must hold offsets[groups] rows")
+    elif ri.size < used or (used and (ri[:used].min() < 0 or ri[:used].max() >= aq.shape[0])):
+        raise ValueError("row_index must hold offsets[groups] indices inside A")
     y = np.full((m_total, n), np.nan, np.float64)
     bound = np.full((m_total, n), np.nan, np.float64)
     lib().oracle_grouped_gemm(_p(aq), _p(asb), _p(as_), _p(ri), _p(off), groups, _p(bq), _p(bsb),

@@ -264,3 +264,64 @@ def test_grouped_config5_down():
     y = nv.nvfp4_grouped_gemm(dev_op(a), to_dev(offsets), dev_op(b))
     y_ref, bound = oracle.grouped_gemm(a, offsets, b)
     check_gemm(to_np(y), y_ref, bound, "config 5 down (all entries)")
+
+
+def _random_k(rng):
+    # k % 256 == 0 (LDS-staged, and the few-rows kernel), other multiples of
+    # 128 (register-direct) and of 16 (masked), up to 4096
+    kind = int(rng.integers(0, 3))
+    if kind == 0:
+        return 256 * int(rng.integers(1, 17))
+    if kind == 1:
+        return 128 * (2 * int(rng.integers(0, 16)) + 1)
+    return 16 * int(rng.integers(1, 257))
+
+
+def test_dense_random_shapes():
+    """A seeded sweep of 24 dense shapes: m from 1 to 900 (the few-rows
+    kernel up to 64 rows when k % 256 == 0, tiled kernels above, with half
+    tiles and ragged tails), n from 1 to 900, k as in _random_k; every entry
+    within 1e-5 * sum_k |a_k b_k| of the oracle."""
+    rng = np.random.default_rng(20261204)
+    for case in range(24):
+        m = int(rng.integers(1, 65)) if case % 3 == 0 else int(rng.integers(1, 901))
+        n = int(rng.integers(1, 901))
+        k = _random_k(rng)
+        a, b = quant_pair(3000 + case, m, n, k)
+        y = nv.nvfp4_gemm(dev_op(a), (to_dev(b[0][0]), to_dev(b[1][0]), to_dev(b[2])))
+        y_ref, bound = oracle.gemm(a, (b[0][0], b[1][0], b[2]))
+        check_gemm(y, y_ref, bound, "case %d: %dx%dx%d" % (case, m, n, k))
+
+
+def test_grouped_random_layouts():
+    """A seeded sweep of 16 grouped layouts: 1 to 40 experts with 0 to 300
+    rows each (some layouts at most 16 rows per expert on average, the
+    few-rows kernel when k % 256 == 0), n from 1 to 700, k as in _random_k,
+    gathered rows with a few indices outside A; every entry of the rows the
+    experts own within the bound, and the rows past offsets[groups] of a
+    taller output left untouched."""
+    rng = np.random.default_rng(20261205)
+    for case in range(16):
+        groups = int(rng.integers(1, 41))
+        hi = 17 if case % 2 == 0 else 301
+        counts = rng.integers(0, hi, groups)
+        counts[rng.integers(0, groups)] += 1  # at least one row
+        n = int(rng.integers(1, 701))
+        # the sparse layouts with k % 256 == 0, so they take the few-rows kernel
+        k = 256 * int(rng.integers(1, 17)) if case % 2 == 0 else _random_k(rng)
+        tokens = int(rng.integers(1, 400))
+        n = max(1, min(n, int(1.5e9 // (int(counts.sum()) * k))))  # bounds the oracle's work
+        a, b, offsets, _ = grouped_case(3100 + case, tokens, list(counts), n, k, row_index=False)
+        m_total = int(offsets[-1])
+        ri = rng.integers(0, tokens, m_total).astype(np.int32)
+        ri[rng.random(m_total) < 0.02] = tokens + 5  # outside A: a zero row
+        y = torch.full((m_total + 2, n), float("nan"), device=dev())
+        nv.nvfp4_grouped_gemm(dev_op(a), to_dev(offsets), dev_op(b), row_index=to_dev(ri),
+                              m_total=m_total, out=y)
+        y = to_np(y)
+        bad = ri >= tokens
+        assert np.all(y[:m_total][bad] == 0), "rows gathered from outside A must be zero"
+        y_ref, bound = oracle.grouped_gemm(a, offsets, b, row_index=np.where(bad, 0, ri))
+        check_gemm(y[:m_total][~bad], y_ref[~bad], bound[~bad], "case %d: %d groups, %d rows, n=%d k=%d" % (
+            case, groups, m_total, n, k))
+        assert np.all(np.isnan(y[m_total:]))

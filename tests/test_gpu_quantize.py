@@ -122,6 +122,44 @@ def test_quantize_rows_ragged_counts(rows):
                           "rows=%d k=%d" % (rows, k))
 
 
+# The smallest and largest K (at most 8192) of every row layout the row
+# kernels select (L lanes per row x U half-blocks per lane: L = 16 for K up
+# to 240 and 384..1920 when the half-blocks divide by 16 only, L = 32 when
+# they divide by 32 only, L = 64 otherwise; U from 1 to 16), and two K past
+# 8192 (the long-row kernel).
+LAYOUT_K = [16, 128, 144, 240, 384, 640, 896, 1152, 1408, 1664, 1920,
+            256, 272, 496, 768, 1280, 1792, 2304, 2816, 3328, 3840,
+            512, 528, 1024, 1040, 1536, 1552, 2048, 2064, 2560, 2576, 3072, 3088, 4096,
+            4112, 5120, 5136, 6144, 6160, 8192, 8208, 9456]
+
+
+def _spread_rows(seed, rows, k):
+    """Student-t rows, each scaled by its own power of two from 2^-40 to
+    2^40 (exact in bf16), so the outer scales span many exponents."""
+    x = sg.bf16_to_f32(sg.student_t3_bf16(seed, 1, (rows, k)))
+    e = (sg.uniform(seed, 2, rows) * 81).astype(np.int64) - 40
+    return sg.f32_to_bf16(x * np.exp2(e.astype(np.float32))[:, None])
+
+
+@pytest.mark.parametrize("k", LAYOUT_K)
+def test_every_row_layout_all_modes(k):
+    """Each layout in the three modes: row amax, supplied amax (the exact row
+    amax, as a producer would reuse it) and weights (one group of all rows,
+    and groups of one row each); 257 rows, so the last block's row groups
+    are partial."""
+    rows = 257
+    x = _spread_rows(4000 + k, rows, k)
+    xd = to_dev(x)
+    assert_same_quant(nv.nvfp4_quantize_rows(xd), oracle.quantize_rows(x), "rows k=%d" % k)
+    amax = np.abs(sg.bf16_to_f32(x)).max(axis=1).astype(np.float32)
+    assert_same_quant(nv.nvfp4_quantize_rows(xd, amax_in=to_dev(amax)),
+                      oracle.quantize_rows(x, amax_in=amax), "amax_in k=%d" % k)
+    for shape in ((1, rows, k), (rows, 1, k)):
+        w = x.reshape(shape)
+        assert_same_quant(nv.nvfp4_quantize_weight(to_dev(w)), oracle.quantize_weight(w),
+                          "weight %s" % (shape,))
+
+
 def test_quantize_rows_k0_and_empty():
     x = torch.empty((5, 0), dtype=torch.int16, device=dev())
     q, sb, s = nv.nvfp4_quantize_rows(x)

@@ -136,6 +136,27 @@ def test_grouped_without_row_index_reads_rows_in_place(oracle, synth):
     assert np.array_equal(y, y2)
 
 
+def test_grouped_rejects_metadata_outside_its_preconditions(oracle, synth):
+    """The reference reads A rows through row_index and writes the rows the
+    offsets own: indices outside A, decreasing offsets or offsets past the
+    output are rejected instead of read or written out of bounds."""
+    import pytest
+    groups, n, k, tokens = 3, 8, 64, 10
+    a, b, offsets, row_index = _grouped_inputs(oracle, synth, 14, tokens, groups, n, k,
+                                               counts=np.array([4, 5, 3]))
+    for bad in (-1, tokens):
+        ri = row_index.copy()
+        ri[5] = bad
+        with pytest.raises(ValueError):
+            oracle.grouped_gemm(a, offsets, b, row_index=ri)
+    with pytest.raises(ValueError):
+        oracle.grouped_gemm(a, np.array([0, 6, 4, 12], np.int32), b, row_index=row_index)
+    with pytest.raises(ValueError):
+        oracle.grouped_gemm(a, offsets, b, row_index=row_index, m_total=int(offsets[-1]) - 1)
+    with pytest.raises(ValueError):  # without row_index the rows read are 0..offsets[-1]-1
+        oracle.grouped_gemm((a[0][:5], a[1][:5], a[2][:5]), offsets, b)
+
+
 def test_acceptance_rule(oracle):
     y_ref = np.array([1.0, -2.0, 0.0])
     bound = np.array([10.0, 10.0, 0.0])
