@@ -36,6 +36,28 @@ def test_dequantize_random_rows(rows, k):
     check(q, sb, s, what="rows=%d k=%d" % (rows, k))
 
 
+# One K per dequantize layout (16, 32 or 64 lanes per row x 1 to 8
+# half-blocks per lane where the half-blocks divide evenly; the general
+# kernel for the rest), the general kernel also at small, odd and large K.
+DEQ_LAYOUT_K = [16, 128, 384, 640, 144, 256, 768, 1280, 512, 1024, 1536, 2048, 2560, 3072,
+                272, 400, 4096, 4112, 8192, 12304]
+
+
+@pytest.mark.parametrize("k", DEQ_LAYOUT_K)
+def test_dequantize_every_layout(k):
+    """130 rows (partial row groups in the last block), each scaled by its own
+    power of two from 2^-40 to 2^40 before quantizing; per-token scales, and
+    one outer scale per 13 rows (the weight form)."""
+    rows = 130
+    x = sg.bf16_to_f32(sg.student_t3_bf16(5000 + k, sg.S_X, (rows, k)))
+    e = (sg.uniform(5000 + k, 2, rows) * 81).astype(np.int64) - 40
+    x = sg.f32_to_bf16(x * np.exp2(e.astype(np.float32))[:, None])
+    q, sb, s = oracle.quantize_rows(x)
+    check(q, sb, s, what="k=%d" % k)
+    w = oracle.quantize_weight(x.reshape(10, 13, k))
+    check(w[0], w[1], w[2], rows_per_scale=13, what="weight k=%d" % k)
+
+
 def test_dequantize_every_scale_and_code():
     """All 127 finite block-scale codes x all 16 element codes, under outer
     scales with few significant bits (frequent ties), ordinary ones, tiny

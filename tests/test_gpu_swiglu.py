@@ -54,7 +54,11 @@ def check_against_oracle(gu, r, what):
 
 
 @pytest.mark.parametrize("rows,f", [(1, 16), (5, 48), (64, 256), (33, 768), (7, 1040), (16, 2048),
-                                    (9, 2064), (4, 4096), (3, 9728), (2, 12288)])
+                                    (9, 2064), (4, 4096), (3, 9728), (2, 12288),
+                                    # the other kernel sizes: one wave per row (256 columns a
+                                    # step) up to 2048, four waves per row (1024 a step) above
+                                    (6, 512), (5, 528), (4, 1024), (3, 1536), (3, 1792),
+                                    (5, 5120), (3, 6144), (2, 7168), (3, 8192), (2, 9216), (2, 11264)])
 def test_swiglu_quantize_matches_oracle(rows, f):
     gu = gate_up_input(rows, f, seed=1000 + f + rows)
     check_against_oracle(gu, run_all(gu), "rows=%d f=%d" % (rows, f))
