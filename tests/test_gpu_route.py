@@ -29,7 +29,9 @@ def check_route(lg, topk, what):
 
 @pytest.mark.parametrize("T,E,topk", [(1, 8, 1), (7, 16, 4), (64, 128, 8), (4096, 128, 8),
                                       (300, 256, 8), (1000, 1024, 16), (513, 64, 64),
-                                      (20000, 128, 8), (129, 3, 2)])
+                                      (20000, 128, 8), (129, 3, 2),
+                                      # the 17-32 and 257-512 expert kernels
+                                      (77, 20, 3), (50, 32, 4), (333, 512, 8), (100, 300, 16)])
 def test_route_matches_oracle(T, E, topk):
     lg = sg.router_logits(sg.config_seed(50) + T + E, T, E)
     check_route(lg, topk, "T=%d E=%d topk=%d" % (T, E, topk))
