@@ -744,7 +744,8 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f16 MFMA on exactly decoded nvfp4 operands, f32 accumulate; f32 scale math",
+        "dtype": "f16",
+        "dtype_detail": "f16 MFMA on exactly decoded nvfp4 operands, f32 accumulate; f32 scale math",
         "data": "synthetic (seeded: Student-t(3) activations, N(0,0.02) weights, Zipf(1.1) top-8 routing)",
         "config": {
             "workload": "Qwen3-4B-shaped dense linear 4096x2560->9728 + Qwen3-30B-A3B-shaped MoE "
