@@ -126,10 +126,12 @@ __device__ __forceinline__ int64_t gathered_row(const int32_t* row_index, int64_
 
 // Blocks are dealt round-robin to the 8 XCDs (block b runs on XCD b % 8);
 // each XCD owns one region of an (8 / xcd_n) x xcd_n split of the tile grid
-// so its L2 holds that region's A rows and B columns.  Inside a region, n runs
-// fastest.  Grouped: every block derives the per-expert m-tile prefix from the
-// device offsets (a wave scan, in registers for up to 256 experts, else into
-// s_prefix) and finds its expert by a ballot count.
+// so its L2 holds that region's A rows and B columns.  Inside a region,
+// grouped GEMMs run n fastest (an expert's m-tiles share its B panels);
+// dense GEMMs run bands of 8 m-tiles, m fastest within a band.  Grouped:
+// every block derives the per-expert m-tile prefix from the device offsets
+// (a wave scan, in registers for up to 256 experts, else into s_prefix) and
+// finds its expert by a ballot count.
 // Returns false when the block has no tile (block-uniform).  Called by the
 // whole block (one wave of 64 lanes).
 template <int BM, int BN>
@@ -236,8 +238,15 @@ __device__ __forceinline__ bool schedule_tile(const TileGrid& t, int lane,
     const int mpx = (tiles_m + XM - 1) / XM;
     const int mcount = min(mpx, max(tiles_m - xm * mpx, 0));
     if (!place(mcount, jf, hf)) return false;  // block-uniform
-    mt = xm * mpx + jf / width;
-    nt = nlo + jf % width;
+    // bands of 8 m-tiles, every n-tile of the region per band, the band's
+    // m-tiles fastest: an XCD's concurrent tiles then share fewer A rows and
+    // B columns between them (4096 x 9728 x 2560: about 1% faster than n
+    // fastest over the whole region)
+    constexpr int GM = 8;
+    const int band = jf / (GM * width), within = jf % (GM * width);
+    const int bh = min(GM, mcount - band * GM);
+    mt = xm * mpx + band * GM + within % bh;
+    nt = nlo + within / bh;
     row_lo = (int64_t)mt * BM;
     row_hi = min(t.m_total, row_lo + BM);
   }
