@@ -798,7 +798,7 @@ template <int TM, int TN>
 static void launch_gemm_rd(const GemmArgs& a, bool grouped, hipStream_t stream) {
   constexpr int BM = 32 * TM, BN = 32 * TN;
   GemmArgs p = a;
-  const int64_t blocks = plan_tiles<BM, BN>(p.t, p.n, grouped);
+  const int64_t blocks = plan_tiles<BM, BN>(p.t, p.n, grouped, 4, p.row_index != nullptr);
   const bool fast = (p.k % BK) == 0 && nvfp4host::aligned(p.a_q, 16) &&
                     nvfp4host::aligned(p.b_q, 16) && nvfp4host::aligned(p.a_sb, 4) &&
                     nvfp4host::aligned(p.b_sb, 4);

@@ -270,16 +270,26 @@ static inline double split_fill(int64_t tiles, int parts) {
 
 // Host launch plan for BM x BN tiles, `per_cu` blocks resident per CU (4
 // one-wave blocks, or 1 four-wave block): fills tiles_n, xcd_n and slots and
-// returns the number of blocks to launch.
+// returns the number of blocks to launch.  `gathered`: a grouped GEMM reads
+// its A rows through row_index.
 template <int BM, int BN>
-static int64_t plan_tiles(TileGrid& t, int64_t n, bool grouped, int per_cu = 4) {
+static int64_t plan_tiles(TileGrid& t, int64_t n, bool grouped, int per_cu = 4, bool gathered = true) {
   t.tiles_n = (int)((n + BN - 1) / BN);
   // upper bound on m-tiles (grouped: each group adds at most a partial tile;
   // the exact count is derived on the device from the offsets)
   const int64_t tiles_m = (t.m_total + BM - 1) / BM + (grouped ? t.groups : 0);
-  // XCD split: grouped GEMMs split along M (B changes along M); dense GEMMs
-  // take the split with the best balance, preferring more N regions.
+  // XCD split: grouped GEMMs split along M (B changes along M; an expert's
+  // m-tiles share its B panels in one L2); dense GEMMs take the split with
+  // the best balance, preferring more N regions.  A grouped GEMM that reads
+  // A in place (no row_index) splits into 2 M halves x 4 N slices when N
+  // divides evenly: an M range of partial and full expert tiles costs
+  // unevenly (measured on the Zipf-routed down projection: the costliest of
+  // 8 M regions holds 12% more work than the mean, 2.5% with 4 N slices), and
+  // re-reading contiguous A rows once per N slice is cheap.  Gathered A rows
+  // are scattered, and re-reading them cost more than the balance gained
+  // (up projection +3%, down projection -3%).
   t.xcd_n = 1;
+  if (grouped && !gathered && split_fill(t.tiles_n, 4) >= 0.9) t.xcd_n = 4;
   if (!grouped) {
     double best = -1.0;
     for (int xn = 1; xn <= 8; xn *= 2) {

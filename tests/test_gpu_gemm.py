@@ -193,6 +193,19 @@ def test_grouped_without_row_index():
     check_gemm(to_np(y)[:m], y_ref[:m], bound[:m], "grouped, rows in place")
 
 
+@pytest.mark.parametrize("n,k", [(512, 768), (1000, 256), (2048, 512)])
+def test_grouped_in_place_split_into_column_slices(n, k):
+    """A grouped GEMM without row_index and at least 4 column tiles runs its
+    XCD regions as 2 row halves x 4 column slices: uneven experts (empty,
+    one-slab, several tiles) with a ragged last column tile at n = 1000;
+    every entry against the oracle."""
+    counts = [300, 0, 17, 129, 1, 64, 0, 250, 33, 96, 5, 400]
+    a, b, offsets, _ = grouped_case(61 + n, sum(counts), counts, n, k, row_index=False)
+    y = to_np(nv.nvfp4_grouped_gemm(dev_op(a), to_dev(offsets), dev_op(b)))
+    y_ref, bound = oracle.grouped_gemm(a, offsets, b)
+    check_gemm(y, y_ref, bound, "grouped in place n=%d k=%d" % (n, k))
+
+
 def test_grouped_single_expert_matches_dense():
     a, b = quant_pair(12, 300, 256, 1024)
     ad, bd = dev_op(a), dev_op(b)
