@@ -21,6 +21,7 @@ struct TileGrid {
   int groups;               // grouped only
   int tiles_n;
   int xcd_n;  // XCD regions along N (8 / xcd_n along M)
+  int cost_split;  // grouped, up to 256 experts: M regions bounded by estimated tile cost
   int slots;  // blocks that run at once on one XCD
 };
 
@@ -53,6 +54,12 @@ __device__ __forceinline__ int32_t wave_incl_scan(int32_t v) {
   v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false);  // row_bcast:15
   v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false);  // row_bcast:31
   return v;
+}
+
+// Sum over the 64 lanes of a wave (every lane gets it).
+__device__ __forceinline__ int32_t wave_sum_i32(int32_t v) {
+  v = wave_incl_scan(v);
+  return __builtin_amdgcn_readlane(v, 63);
 }
 
 template <int BM>
@@ -200,10 +207,50 @@ __device__ __forceinline__ bool schedule_tile(const TileGrid& t, int lane,
       carry += __builtin_amdgcn_readlane(incl, 63);
     }
     const int total_mt = carry;
-    const int mpx = (total_mt + XM - 1) / XM;
-    const int mcount = min(mpx, max(total_mt - xm * mpx, 0));
+    int m0, mcount;
+    if (t.cost_split) {
+      // Regions of equal estimated cost rather than equal m-tile counts: a
+      // partial expert tile runs fewer 32-row slabs but streams and decodes
+      // the same B panel.  Costs in 1/20 of a full tile, from per-block
+      // timing stamps (a full tile 20; 1, 2, 3 valid slabs 10, 13, 17).  A
+      // region holds the m-tiles whose starting cost falls in its 1/XM of
+      // the total, in expert order.
+      int32_t cx[4] = {0, 0, 0, 0}, cn[4] = {0, 0, 0, 0};
+      int64_t ccarry = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (64 * i >= G) break;
+        const int e = 64 * i + lane;
+        const int32_t rows = hi[i] - lo[i];
+        const int32_t full = rows / BM, rem = rows - full * BM;
+        const int32_t v = (rem + 31) / 32;
+        const int32_t w = v == 0 ? 0 : (v == 1 ? 10 : (v == 2 ? 13 : 17));
+        const int32_t ce = e < G ? 20 * full + w : 0;
+        const int32_t incl = wave_incl_scan(ce);
+        cx[i] = (int32_t)ccarry + incl - ce;
+        cn[i] = e < G ? full + (v > 0 ? 1 : 0) : 0;
+        ccarry += __builtin_amdgcn_readlane(incl, 63);
+      }
+      auto tiles_before = [&](int64_t bound) -> int {
+        int32_t s = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          if (64 * i >= G) break;
+          const int64_t d = bound - cx[i];
+          const int32_t tb = d <= 0 ? 0 : (int32_t)min((d + 19) / 20, (int64_t)cn[i]);
+          s += tb;
+        }
+        return wave_sum_i32(s);
+      };
+      m0 = tiles_before(ccarry * xm / XM);
+      mcount = tiles_before(ccarry * (xm + 1) / XM) - m0;
+    } else {
+      const int mpx = (total_mt + XM - 1) / XM;
+      m0 = xm * mpx;
+      mcount = min(mpx, max(total_mt - xm * mpx, 0));
+    }
     if (!place(mcount, jf, hf)) return false;  // block-uniform
-    mt = xm * mpx + jf / width;
+    mt = m0 + jf / width;
     nt = nlo + jf % width;
     int count = 0;
 #pragma unroll
@@ -289,7 +336,13 @@ static int64_t plan_tiles(TileGrid& t, int64_t n, bool grouped, int per_cu = 4, 
   // are scattered, and re-reading them cost more than the balance gained
   // (up projection +3%, down projection -3%).
   t.xcd_n = 1;
+  t.cost_split = 0;
   if (grouped && !gathered && split_fill(t.tiles_n, 4) >= 0.9) t.xcd_n = 4;
+  // Gathered grouped GEMMs (the up projection) keep whole M regions and
+  // bound them by estimated cost instead (the schedule's register path, up
+  // to 256 experts; the 128-row tile kernels, which run only a partial
+  // tile's valid slabs): up projection 3.5% faster in same-box pairs.
+  if (grouped && gathered && t.groups <= 256 && BM == 128) t.cost_split = 1;
   if (!grouped) {
     double best = -1.0;
     for (int xn = 1; xn <= 8; xn *= 2) {
@@ -299,9 +352,11 @@ static int64_t plan_tiles(TileGrid& t, int64_t n, bool grouped, int per_cu = 4, 
   }
   t.slots = (nvfp4host::num_cus() / 8) * per_cu;
   if (t.slots < 2) t.slots = 2;
-  const int64_t per_xcd = ((tiles_m + (8 / t.xcd_n) - 1) / (8 / t.xcd_n)) *
-                              ((t.tiles_n + t.xcd_n - 1) / t.xcd_n) +
-                          t.slots / 2;  // room for the split tail
+  // a cost-bounded region holds at most twice the mean m-tile count (no
+  // tile costs less than half a full one), plus one
+  const int64_t mreg = t.cost_split ? 2 * ((tiles_m + (8 / t.xcd_n) - 1) / (8 / t.xcd_n)) + 1
+                                    : (tiles_m + (8 / t.xcd_n) - 1) / (8 / t.xcd_n);
+  const int64_t per_xcd = mreg * ((t.tiles_n + t.xcd_n - 1) / t.xcd_n) + t.slots / 2;  // room for the split tail
   return 8 * per_xcd;
 }
 
