@@ -40,6 +40,9 @@
  *     current device is not gfx950.
  *   - Alignment: tensor pointers must be 16-byte aligned (fp32 scale
  *     vectors 4-byte aligned).
+ *   - GEMM sizes: besides each call's own limits, an output whose tile grid
+ *     ((m_total / 128 + groups + 1) x (n / 64 + 1)) passes 2^28 tiles -- far
+ *     beyond device memory -- is rejected with UNSUPPORTED_SHAPE.
  *   - Inputs must be finite; non-finite bf16 inputs give unspecified codes
  *     (no fault).  Stateless and re-entrant; calls on one stream are ordered.
  *   - Device-side preconditions (values in device memory, which the host

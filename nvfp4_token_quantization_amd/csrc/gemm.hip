@@ -832,7 +832,8 @@ extern "C" int nvfp4_gemm(const uint8_t* a_q, const uint8_t* a_sb, const float* 
   if (m == 0 || n == 0) return NVFP4_SUCCESS;
   if (!y || !a_s || !b_s) return NVFP4_ERROR_INVALID_VALUE;
   if (k > 0 && (!a_q || !a_sb || !b_q || !b_sb)) return NVFP4_ERROR_INVALID_VALUE;
-  if (m > ((int64_t)1 << 31) || n > ((int64_t)1 << 31) || k > ((int64_t)1 << 24))
+  if (m > ((int64_t)1 << 31) || n > ((int64_t)1 << 31) || k > ((int64_t)1 << 24) ||
+      !nvfp4::tile_grid_ok(m, 0, n))
     return NVFP4_ERROR_UNSUPPORTED_SHAPE;
   if (!aligned(a_q, 16) || !aligned(b_q, 16) || !aligned(a_sb, 16) || !aligned(b_sb, 16) ||
       !aligned(y, 16) || !aligned(a_s, 4) || !aligned(b_s, 4))
@@ -875,7 +876,7 @@ extern "C" int nvfp4_grouped_gemm(const uint8_t* a_q, const uint8_t* a_sb, const
   if (k > 0 && a_rows > 0 && (!a_q || !a_sb)) return NVFP4_ERROR_INVALID_VALUE;
   if (k > 0 && (!b_q || !b_sb)) return NVFP4_ERROR_INVALID_VALUE;
   if (m_total > ((int64_t)1 << 31) || a_rows > ((int64_t)1 << 31) || n > ((int64_t)1 << 31) ||
-      k > ((int64_t)1 << 24))
+      k > ((int64_t)1 << 24) || !nvfp4::tile_grid_ok(m_total, groups, n))
     return NVFP4_ERROR_UNSUPPORTED_SHAPE;
   if (!aligned(a_q, 16) || !aligned(b_q, 16) || !aligned(a_sb, 16) || !aligned(b_sb, 16) ||
       !aligned(y, 16) || !aligned(a_s, 4) || !aligned(b_s, 4) || !aligned(offsets, 4) ||
@@ -918,7 +919,7 @@ extern "C" int nvfp4_grouped_gemm_swiglu(const uint8_t* a_q, const uint8_t* a_sb
   if (!row_index && a_rows < m_total) return NVFP4_ERROR_INVALID_VALUE;
   const int64_t lim = (int64_t)1 << 31;
   if (m_total > lim || a_rows > lim || 2 * f >= ((int64_t)1 << 22) || k > ((int64_t)1 << 24) ||
-      a_rows * (k / 2) >= lim || 2 * f * (k / 2) >= lim)
+      a_rows * (k / 2) >= lim || 2 * f * (k / 2) >= lim || !nvfp4::tile_grid_ok(m_total, groups, f))
     return NVFP4_ERROR_UNSUPPORTED_SHAPE;
   if (!aligned(a_q, 16) || !aligned(b_q, 16) || !aligned(a_sb, 16) || !aligned(b_sb, 16) ||
       !aligned(a_s, 4) || !aligned(b_s, 4) || !aligned(offsets, 4) || !aligned(row_index, 4) ||

@@ -252,7 +252,8 @@ extern "C" int nvfp4_mxfp8_gemm(const uint8_t* a_q, const uint8_t* a_sc, int64_t
   if (k % 32 != 0) return NVFP4_ERROR_UNSUPPORTED_SHAPE;
   if (m == 0 || n == 0) return NVFP4_SUCCESS;
   if (!y || (k > 0 && (!a_q || !a_sc || !b_q || !b_sc))) return NVFP4_ERROR_INVALID_VALUE;
-  if (m > ((int64_t)1 << 31) || n > ((int64_t)1 << 31) || k > ((int64_t)1 << 24))
+  if (m > ((int64_t)1 << 31) || n > ((int64_t)1 << 31) || k > ((int64_t)1 << 24) ||
+      !nvfp4::tile_grid_ok(m, 0, n))
     return NVFP4_ERROR_UNSUPPORTED_SHAPE;
   if (!aligned(a_q, 16) || !aligned(b_q, 16) || !aligned(y, 16)) return NVFP4_ERROR_MISALIGNED;
   int st = nvfp4host::check_arch();
@@ -288,7 +289,7 @@ extern "C" int nvfp4_mxfp8_grouped_gemm(const uint8_t* a_q, const uint8_t* a_sc,
   if (k > 0 && a_rows > 0 && (!a_q || !a_sc)) return NVFP4_ERROR_INVALID_VALUE;
   if (k > 0 && (!b_q || !b_sc)) return NVFP4_ERROR_INVALID_VALUE;
   if (m_total > ((int64_t)1 << 31) || a_rows > ((int64_t)1 << 31) || n > ((int64_t)1 << 31) ||
-      k > ((int64_t)1 << 24))
+      k > ((int64_t)1 << 24) || !nvfp4::tile_grid_ok(m_total, groups, n))
     return NVFP4_ERROR_UNSUPPORTED_SHAPE;
   if (!aligned(a_q, 16) || !aligned(b_q, 16) || !aligned(y, 16) || !aligned(offsets, 4) ||
       !aligned(row_index, 4))

@@ -309,6 +309,14 @@ __device__ __forceinline__ bool schedule_tile(const TileGrid& t, int lane,
   return true;
 }
 
+// Host check that a tiled launch's grid stays far below 2^31 blocks (tile
+// indices are 32-bit, and a cost-bounded grouped plan launches up to twice
+// the tiles): at most 2^28 tiles of 128 x 64 over the output rows plus one
+// partial tile per group.  Only outputs far beyond device memory fail it.
+static inline bool tile_grid_ok(int64_t m_total, int64_t groups, int64_t n) {
+  return ((m_total + 127) / 128 + groups + 1) * ((n + 63) / 64 + 1) <= ((int64_t)1 << 28);
+}
+
 // Fill of an even split of `tiles` into `parts` ranges (1.0 = balanced).
 static inline double split_fill(int64_t tiles, int parts) {
   const int64_t per = (tiles + parts - 1) / parts;

@@ -151,6 +151,21 @@ def test_grouped_gemm_argument_errors(L):
     assert f(None, None, None, 0, None, 0, None, 2, None, None, None, 8, 16, None, None) == OK
 
 
+def test_gemm_grids_past_the_tile_limit(L):
+    """Outputs whose tile grid would pass 2^28 tiles (far beyond device
+    memory) are rejected as UNSUPPORTED_SHAPE before any HIP call, in every
+    tiled GEMM entry point; the largest sizes each argument allows on its
+    own still pass the other checks."""
+    a = P(FAKE)
+    big = 1 << 31
+    assert L.nvfp4_gemm(a, a, a, big, a, a, a, big, 16, a, None) == SHAPE
+    assert L.nvfp4_grouped_gemm(a, a, a, big, a, big, a, 4, a, a, a, big, 16, a, None) == SHAPE
+    assert L.nvfp4_grouped_gemm_swiglu(a, a, a, 64, a, big, a, 4, a, a, a, (1 << 21) - 16, 256,
+                                       a, a, None) == SHAPE
+    assert L.nvfp4_mxfp8_gemm(a, a, big, a, a, big, 32, a, None) == SHAPE
+    assert L.nvfp4_mxfp8_grouped_gemm(a, a, big, a, big, a, 4, a, a, big, 32, a, None) == SHAPE
+
+
 def test_swiglu_quantize_argument_errors(L):
     f = L.nvfp4_swiglu_quantize_rows
     a = P(FAKE)
