@@ -212,7 +212,8 @@ __device__ __forceinline__ bool schedule_tile(const TileGrid& t, int lane,
       // Regions of equal estimated cost rather than equal m-tile counts: a
       // partial expert tile runs fewer 32-row slabs but streams and decodes
       // the same B panel.  Costs in 1/20 of a full tile, from per-block
-      // timing stamps (a full tile 20; 1, 2, 3 valid slabs 10, 13, 17).  A
+      // timing stamps (4 valid slabs, full or not, 20; 1, 2, 3 slabs 10, 13,
+      // 17).  A
       // region holds the m-tiles whose starting cost falls in its 1/XM of
       // the total, in expert order.
       int32_t cx[4] = {0, 0, 0, 0}, cn[4] = {0, 0, 0, 0};
@@ -224,7 +225,7 @@ __device__ __forceinline__ bool schedule_tile(const TileGrid& t, int lane,
         const int32_t rows = hi[i] - lo[i];
         const int32_t full = rows / BM, rem = rows - full * BM;
         const int32_t v = (rem + 31) / 32;
-        const int32_t w = v == 0 ? 0 : (v == 1 ? 10 : (v == 2 ? 13 : 17));
+        const int32_t w = v == 0 ? 0 : (v == 1 ? 10 : (v == 2 ? 13 : (v == 3 ? 17 : 20)));
         const int32_t ce = e < G ? 20 * full + w : 0;
         const int32_t incl = wave_incl_scan(ce);
         cx[i] = (int32_t)ccarry + incl - ce;
