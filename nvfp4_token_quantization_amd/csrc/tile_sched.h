@@ -213,9 +213,8 @@ __device__ __forceinline__ bool schedule_tile(const TileGrid& t, int lane,
       // partial expert tile runs fewer 32-row slabs but streams and decodes
       // the same B panel.  Costs in 1/20 of a full tile, from per-block
       // timing stamps (4 valid slabs, full or not, 20; 1, 2, 3 slabs 10, 13,
-      // 17).  A
-      // region holds the m-tiles whose starting cost falls in its 1/XM of
-      // the total, in expert order.
+      // 17).  A region holds the m-tiles whose starting cost falls in its
+      // 1/XM of the total, in expert order.
       int32_t cx[4] = {0, 0, 0, 0}, cn[4] = {0, 0, 0, 0};
       int64_t ccarry = 0;
 #pragma unroll
